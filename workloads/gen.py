@@ -1,0 +1,87 @@
+"""Seeded random draws for the paged-decode workloads.
+
+Every array comes from ``numpy.random.default_rng([seed, tag, ...])`` so that a
+piece of data (one sequence's keys and values, one step's queries) can be
+regenerated on its own, in any order, and always gives the same bits.  Values
+are standard normal; bf16 data is the float32 draw rounded to nearest-even and
+returned as raw ``uint16`` bit patterns, float32 data is returned as float32.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Sub-stream tags: the second word of every seed sequence.
+TAG_CTX = 1      # context lengths
+TAG_PERM = 2     # permutation of the physical block pool (free-list order)
+TAG_Q = 3        # queries, per decode step
+TAG_KV = 4       # per-sequence key/value history, per token position
+TAG_NEW = 5      # keys/values of the tokens written by a decode step
+TAG_TRACE = 6    # arrivals / prompt lengths / output lengths of a serving trace
+
+DTYPES = ("f32", "bf16")
+
+
+def stream(seed: int, *tags: int) -> np.random.Generator:
+    """Independent generator for (seed, tags...)."""
+    return np.random.default_rng([int(seed), *[int(t) for t in tags]])
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to bfloat16, nearest-even; return uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def draw_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """Standard-normal draw in the storage format of ``dtype``."""
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return x if dtype == "f32" else bf16_bits_from_f32(x)
+
+
+def seq_kv(seed: int, seq: int, ctx: int, num_kv_heads: int, head_dim: int,
+           dtype: str):
+    """Keys and values of tokens 0..ctx-1 of sequence ``seq``: two [ctx, Hkv, D].
+
+    The draw is prefix-stable: token p has the same value whatever ``ctx`` is,
+    so a sequence that grows (or is recomputed after preemption) rewrites the
+    same bits at the same positions.
+    """
+    rng = stream(seed, TAG_KV, seq)
+    kv = draw_values(rng, (ctx, 2, num_kv_heads, head_dim), dtype)
+    return np.ascontiguousarray(kv[:, 0]), np.ascontiguousarray(kv[:, 1])
+
+
+def new_tokens(seed: int, step: int, num_tokens: int, num_kv_heads: int,
+               head_dim: int, dtype: str):
+    """Keys and values of the tokens a decode step writes: two [T, Hkv, D]."""
+    rng = stream(seed, TAG_NEW, step)
+    kv = draw_values(rng, (num_tokens, 2, num_kv_heads, head_dim), dtype)
+    return np.ascontiguousarray(kv[:, 0]), np.ascontiguousarray(kv[:, 1])
+
+
+def q_values(seed: int, step: int, num_seqs: int, num_q_heads: int,
+             head_dim: int, dtype: str) -> np.ndarray:
+    """Queries of one decode step: [S, Hq, D]."""
+    return draw_values(stream(seed, TAG_Q, step), (num_seqs, num_q_heads, head_dim), dtype)
+
+
+def context_lens_uniform(seed: int, num_seqs: int, lo: int, hi: int) -> np.ndarray:
+    """Context lengths uniform on the integers [lo, hi] (int32)."""
+    return stream(seed, TAG_CTX).integers(lo, hi + 1, num_seqs).astype(np.int32)
+
+
+def context_lens_loguniform(seed: int, num_seqs: int, lo: int, hi: int) -> np.ndarray:
+    """Context lengths log-uniform on [lo, hi], rounded to integers (int32)."""
+    u = stream(seed, TAG_CTX).uniform(np.log(lo), np.log(hi), num_seqs)
+    return np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int32)
+
+
+def pool_permutation(seed: int, num_blocks: int) -> np.ndarray:
+    """A seeded permutation of the physical block IDs 0..N-1 (int32)."""
+    return stream(seed, TAG_PERM).permutation(num_blocks).astype(np.int32)
