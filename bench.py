@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+One step is one pass of the whole decode hot path over the batch:
+  host bookkeeping (library allocator: reserve every sequence's next slot,
+  copy-on-write pairs, changed table entries) -> one host-to-device copy of
+  that metadata -> block copies and table updates -> cache write of the new
+  tokens' K/V -> decode attention (pass 1, then the merge of split sequences).
+All inputs (cache contents, per-step q / k / v) are resident in HBM before the
+timed region.  The host part of step n+1 overlaps the device part of step n.
+
+Prints one JSON line (the benchmark contract) with the whole-step effective
+KV bandwidth as `value`, the pass-1 roofline (HIP events on the launch stream)
+and the CPU oracle timed on a sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + µs/step, batch 256"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gqa_b256",
+                    choices=["gqa_b256", "llama2_7b_b64", "shared_prefix_b16", "shared_prefix_b32"])
+    ap.add_argument("--units", type=int, default=0, help="decode work units (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, ctx, q_host, seconds):
+    """Time the fp64 oracle (as it stands) on every 4th sequence of step 0's batch."""
+    from oracle.attention import paged_decode
+    from oracle.cache import reshape_and_cache
+    from oracle.layout import CacheLayout
+    from workloads import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    sample = list(range(0, len(ctx), 4))
+    B = cfg.block_size
+    nblk = [-(-int(ctx[i]) // B) for i in sample]
+    lay = CacheLayout(sum(nblk), cfg.num_kv_heads, B, cfg.head_dim, cfg.dtype)
+    kc, vc = lay.empty_cache(), lay.empty_cache()
+    tables = np.full((len(sample), max(nblk)), -1, dtype=np.int64)
+    pos = 0
+    for r, i in enumerate(sample):
+        tables[r, :nblk[r]] = np.arange(pos, pos + nblk[r])
+        pos += nblk[r]
+        K, V = gen.seq_kv(cfg.seed, i, int(ctx[i]), cfg.num_kv_heads, cfg.head_dim, cfg.dtype)
+        slots = tables[r, np.arange(int(ctx[i])) // B] * B + np.arange(int(ctx[i])) % B
+        reshape_and_cache(lay, K, V, slots, kc, vc)
+    sctx = ctx[sample]
+    q = q_host[sample]
+    times = []
+    t_end = time.perf_counter() + seconds
+    while not times or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        paged_decode(lay, q, kc, vc, tables, sctx, cfg.scale)
+        times.append(time.perf_counter() - t0)
+    kv_bytes = int(sctx.sum()) * cfg.kv_bytes_per_token()
+    t = float(np.median(times))
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle (gather + textbook softmax) on every 4th sequence of "
+                       f"the batch ({len(sample)} seqs, {int(sctx.sum())} tokens, "
+                       f"{kv_bytes / 1e9:.3f} GB of KV), median of {len(times)} runs"),
+            "seconds_per_run": t, "cpu_model": cpu, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path "
+              f"shards by sequence or KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_397_amd import ops, _native
+    from paged_kv_cache_397_amd.batch import PagedKVCache, to_device
+    from workloads import CONFIGS, gen
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    _native.lib()  # fail loudly if the HIP library is not built
+    cfg = CONFIGS[args.config]
+    spec = ops.CacheSpec(cfg.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_dim, cfg.dtype)
+    S, Hq, Hkv, D, B = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    steps, warm = args.steps, args.warmup
+    total_steps = steps + warm
+
+    # ---------------------------------------------------------------- resident inputs
+    t0 = time.time()
+    cache = PagedKVCache(spec, cfg.pool_order(), fill=0.0)
+    ctx0 = cfg.context_lens()
+    seq_ids = np.arange(S, dtype=np.int64)
+    if cfg.ctx_kind == "shared_prefix":
+        # one parent holds the shared prefix (ending in a partial block); the other
+        # sequences fork it, then every sequence appends its private suffix token by
+        # token, round robin, so each first append meets the shared partial block.
+        prefix = cfg.shared_prefix + B // 2
+        Kp, Vp = gen.seq_kv(cfg.seed, 0, prefix, Hkv, D, cfg.dtype)
+        cache.add_sequence(0, Kp, Vp)
+        for c in range(1, S):
+            cache.alloc.fork(0, c)
+        extra = ctx0.astype(np.int64) - prefix
+        suffix = [gen.seq_kv(cfg.seed, 1000 + i, int(extra[i]), Hkv, D, cfg.dtype) for i in range(S)]
+        written = np.zeros(S, dtype=np.int64)
+        while (written < extra).any():
+            active = np.nonzero(written < extra)[0]
+            st, done, slots, cows, _, _ = cache.alloc.append_batch(active)
+            assert st == 0 and done == len(active)
+            pairs = cows[cows[:, 0] >= 0]
+            if len(pairs):
+                ops.copy_blocks(spec, cache.k, cache.v,
+                                torch.from_numpy(np.ascontiguousarray(pairs)).cuda())
+            kk = np.stack([suffix[i][0][written[i]] for i in active])
+            vv = np.stack([suffix[i][1][written[i]] for i in active])
+            cache.write_tokens(kk, vv, slots)
+            written[active] += 1
+    else:
+        for i in range(S):
+            K, V = gen.seq_kv(cfg.seed, i, int(ctx0[i]), Hkv, D, cfg.dtype)
+            cache.add_sequence(i, K, V)
+            if i % 32 == 31:
+                log(f"cache fill: {i + 1}/{S} sequences")
+    max_blocks = -(-(int(ctx0.max()) + total_steps + 1) // B)
+    tables_h, ctx_h = cache.alloc.batch_metadata(seq_ids, max_blocks)
+    assert np.array_equal(ctx_h, ctx0)
+    tables = torch.from_numpy(tables_h).cuda()
+    q_host0 = gen.q_values(cfg.seed, 0, S, Hq, D, cfg.dtype)
+    qs, ks, vs = [], [], []
+    for n in range(total_steps):
+        qs.append(to_device(gen.q_values(cfg.seed, n + 1, S, Hq, D, cfg.dtype), spec))
+        kn, vn = gen.new_tokens(cfg.seed, n + 1, S, Hkv, D, cfg.dtype)
+        ks.append(to_device(kn, spec))
+        vs.append(to_device(vn, spec))
+    out = torch.empty(S, Hq, D, dtype=spec.torch_dtype, device="cuda")
+    units = args.units if args.units > 0 else ops.default_units()
+    ws = ops.decode_workspace(spec, Hq, units)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM ({time.time() - t0:.1f} s): {S} seqs, sum ctx {int(ctx0.sum())}, "
+        f"{units} units")
+
+    # ---------------------------------------------------------------- per-step staging
+    R = 4  # ring of pinned metadata buffers
+    words = S * 2 + S + 3 * S + 2 * S  # int32 words: slots (int64), ctx, updates, cow pairs
+    pin = [torch.empty(words, dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    dev = [torch.empty(words, dtype=torch.int32, device="cuda") for _ in range(R)]
+    ring_ev = [None] * R
+
+    def views(buf):
+        return (buf[:2 * S].view(torch.int64), buf[2 * S:3 * S], buf[3 * S:6 * S].view(S, 3),
+                buf[6 * S:8 * S].view(S, 2))
+
+    ctx_now = ctx0.astype(np.int64).copy()
+    stream = torch.cuda.current_stream()
+    kv_per_tok = cfg.kv_bytes_per_token()
+    ev = []
+
+    def step(n, timed):
+        # a1: host bookkeeping in the library allocator
+        st, done, slots, cows, nb, nc = cache.alloc.append_batch(seq_ids)
+        if st != 0 or done != S:
+            raise RuntimeError(f"append_batch failed at step {n}: status {st}")
+        ctx_now[:] += 1
+        upd_rows = np.nonzero(nb >= 0)[0]
+        cow_rows = np.nonzero(cows[:, 0] >= 0)[0]
+        # a2: one host-to-device copy of the step's metadata
+        r = n % R
+        if ring_ev[r] is not None:
+            ring_ev[r].synchronize()
+        ps, pc, pu, pp = views(pin[r])
+        ps.numpy()[:] = slots
+        pc.numpy()[:] = ctx_now
+        if len(upd_rows):
+            pu.numpy()[:len(upd_rows)] = np.stack([upd_rows, nc[upd_rows], nb[upd_rows]], 1)
+        if len(cow_rows):
+            pp.numpy()[:len(cow_rows)] = cows[cow_rows]
+        dev[r].copy_(pin[r], non_blocking=True)
+        e = torch.cuda.Event()
+        e.record(stream)
+        ring_ev[r] = e
+        ds, dc, du, dp = views(dev[r])
+        if timed:
+            e_start = torch.cuda.Event(enable_timing=True)
+            e_start.record(stream)
+        # a3: copy-on-write block copies, then the changed table entries
+        if len(cow_rows):
+            ops.copy_blocks(spec, cache.k, cache.v, dp[:len(cow_rows)])
+        if len(upd_rows):
+            ops.update_block_tables(tables, du[:len(upd_rows)])
+        # a4: cache write of the step's new tokens
+        ops.reshape_and_cache(spec, ks[n], vs[n], ds, cache.k, cache.v)
+        # a5-a11: decode attention, pass 1 then the merge
+        if timed:
+            e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e1.record(stream)
+        ops.paged_attn_decode_partial(spec, out, qs[n], cache.k, cache.v, tables, dc, cfg.scale,
+                                      units, ws)
+        if timed:
+            e2.record(stream)
+        ops.paged_attn_decode_merge(spec, out, qs[n], cache.k, cache.v, tables, dc, cfg.scale,
+                                    units, ws)
+        if timed:
+            e3.record(stream)
+            ev.append((e_start, e1, e2, e3, int(ctx_now.sum())))
+
+    for n in range(warm):
+        step(n, False)
+    torch.cuda.synchronize()
+    log(f"warmup done ({warm} steps)")
+    t0 = time.perf_counter()
+    for n in range(warm, total_steps):
+        step(n, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {steps} steps in {wall * 1e3:.2f} ms")
+
+    tok = np.array([e[4] for e in ev], dtype=np.float64)
+    kv_bytes = tok * kv_per_tok
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_p1 = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    t_attn = np.array([e[1].elapsed_time(e[3]) for e in ev]) * 1e-3
+    value = float(kv_bytes.sum() / wall / 1e9)
+    p1_gbps = float(np.median(kv_bytes / t_p1) / 1e9)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.title}", "seqs": S, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "block_size": B, "pool_blocks": cfg.num_blocks,
+                   "sum_ctx_first_step": int(tok[0]), "units": units, "seed": cfg.seed},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "us_per_step": round(wall / steps * 1e6, 2),
+        "device_us_per_step_median": round(float(np.median(t_write + t_attn)) * 1e6, 2),
+        "write_us_median": round(float(np.median(t_write)) * 1e6, 2),
+        "attn_us_median": round(float(np.median(t_attn)) * 1e6, 2),
+        "attn_gbps_median": round(float(np.median(kv_bytes / t_attn) / 1e9), 2),
+        "roofline": {
+            "kernel": "decode_pass1",
+            "bound": "hbm",
+            "achieved": round(p1_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(p1_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "pass1_us_mean": round(float(t_p1.mean()) * 1e6, 2),
+            "pass1_us_median": round(float(np.median(t_p1)) * 1e6, 2),
+            "algorithmic_bytes_per_launch": int(np.median(kv_bytes)),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the batch")
+        result["cpu_baseline"] = cpu_baseline(cfg, ctx0, q_host0, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    result["host"] = {"python": platform.python_version(), "torch": torch.__version__,
+                      "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

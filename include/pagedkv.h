@@ -1,0 +1,265 @@
+/*
+ * pagedkv.h - C ABI of libpagedkv: paged KV-cache decode attention, cache writes
+ * and a host-side block allocator for AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what is computed (restated, not quoted):
+ *   [P1] ksqn.cn "大模型推理性能优化：PagedAttention与Continuous Batching原理与实践"
+ *   [P2] hihuo.com "vLLM 原理：PagedAttention 和 Continuous Batching"
+ *   [P3] blog.gitcode.com "如何通过PagedAttention实现LLM高性能推理：实战指南"
+ *
+ * Every symbol is extern "C"; arguments are plain pointers, integers and one
+ * small descriptor struct.  Device pointers are HIP device addresses owned by
+ * the caller; `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream).  Device calls only enqueue work on that stream and return; the
+ * library never allocates, frees or synchronises device memory.
+ *
+ * Errors: every call returns pa_status (or a documented sentinel) and never
+ * aborts.  Host validation covers what the host can see: null pointers,
+ * negative sizes, unsupported shapes, 16-byte alignment, workspace size,
+ * 32-bit index range.  Values that only the device sees (block IDs, slots,
+ * context lengths) are preconditions; a violation gives unspecified results
+ * but never an out-of-bounds access: the kernels clamp or skip such entries
+ * as stated per call.  A launch failure returns PA_ERR_HIP.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, misalignment, bad struct field */
+    PA_ERR_UNSUPPORTED = 2,  /* valid request outside the compiled shapes / dtypes        */
+    PA_ERR_OOM = 3,          /* allocator: not enough free blocks; state unchanged          */
+    PA_ERR_STATE = 4,        /* allocator: unknown / duplicate / already-freed sequence     */
+    PA_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed                  */
+} pa_status;
+
+typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+
+/*
+ * The physical cache: one K array and one V array, each holding num_blocks
+ * blocks of block_size token slots for num_kv_heads heads of head_dim values
+ * ([P1] section 2.2: fixed-size pages scattered through one pool; [P2]
+ * PagedAttention > 工作原理 > 1. 页表管理: a per-sequence page table).
+ *
+ * Supported: block_size in {16, 32, 64}; head_dim in {64, 128};
+ * dtype in {F32, BF16}.
+ *
+ * Layout (the library's own choice; the pages fix only the logical picture).
+ * Let s = element bytes, X = 16 / s (elements per 16-byte group), E = X / 4,
+ * TPB = block_size / 16.  A block is cut into TPB tiles of 16 tokens; tiles
+ * are ordered block -> kv head -> tile, each tile holding 16 * head_dim
+ * elements.  Element (block b, head h, token slot o, dim d) sits at
+ *
+ *   K: ((((b*Hkv + h)*TPB + o/16)*(D/X) + d/X)*16 + o%16)*X + d%X
+ *   V: ((b*Hkv + h)*TPB + o/16)*16*D
+ *      + ((((d/(16E))*4 + (o%16)/4)*16 + d%16)*E + (d/16)%E)*4 + o%4
+ *
+ * so a K 16-byte group is X consecutive dims of one token, and a V 16-byte
+ * group is 4 consecutive tokens of E dims spaced 16 apart.  One wavefront
+ * reading a tile with one 16-byte load per lane per 1 KiB touches one
+ * contiguous KiB per instruction.
+ *
+ * A slot is b * block_size + o.  Bytes per array: pa_cache_bytes().
+ */
+typedef struct pa_cache_desc {
+    int32_t num_blocks;    /* N > 0                                   */
+    int32_t block_size;    /* B: 16, 32 or 64 tokens per block        */
+    int32_t num_kv_heads;  /* Hkv > 0                                 */
+    int32_t head_dim;      /* D: 64 or 128                            */
+    int32_t dtype;         /* pa_dtype                                */
+} pa_cache_desc;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* pa_status_string(pa_status s);
+
+/* ABI version of this header: (major << 16) | minor. */
+int32_t pa_abi_version(void);
+
+/* Bytes of ONE cache array (K or V) for the descriptor; 0 if the descriptor is invalid. */
+size_t pa_cache_bytes(const pa_cache_desc* desc);
+
+/*
+ * pa_reshape_and_cache - write new tokens' keys and values into their slots.
+ *
+ * The scatter that pairs with the attention gather ([P1] section 2.2) and the
+ * cache update after each forward step ([P2] 调度流程, step 4).
+ *   k, v          device, [num_tokens, Hkv, D] row-major, dtype of the cache, 16-B aligned
+ *   slot_mapping  device, [num_tokens] int64; slot = block * B + offset; -1 = skip
+ *   k_cache, v_cache  device, the cache arrays (layout above), 16-B aligned
+ * Token t's bits are copied unchanged; every other byte of the cache is left
+ * as it was.  Preconditions: no two tokens share a non-negative slot; slots
+ * are < N * B (larger slots are skipped).  num_tokens == 0 is a no-op.
+ */
+pa_status pa_reshape_and_cache(const pa_cache_desc* desc, const void* k, const void* v,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               void* k_cache, void* v_cache, void* stream);
+
+/*
+ * pa_copy_blocks - copy whole physical blocks (K and V, every head and slot).
+ *
+ * Used for copy-on-write of a block shared between sequences ([P2]
+ * PagedAttention > 优势 > 3. 支持共享 names the sharing; the copy before a write
+ * is this library's reading).
+ *   pairs  device, [num_pairs][2] int32 (src, dst)
+ * Pairs run concurrently: no block may be the dst of one pair and the src or
+ * dst of another.  Pairs with an ID outside [0, N) are skipped.
+ */
+pa_status pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache,
+                         const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/*
+ * pa_update_block_tables - apply (row, column, block) updates to a device
+ * block-table array [rows][max_blocks_per_seq] int32.
+ *   updates  device, [num_updates][3] int32; entries with row or column out of
+ *            range are skipped.  Later duplicates of one (row, column) race.
+ * Lets a caller keep the tables resident in HBM and send only the entries the
+ * allocator changed in a step ([P2] 工作原理 > 2. 按需分配: a new page only when a
+ * token crosses a page boundary).
+ */
+pa_status pa_update_block_tables(int32_t* block_tables, int32_t num_rows,
+                                 int32_t max_blocks_per_seq, const int32_t* updates,
+                                 int32_t num_updates, void* stream);
+
+/*
+ * Decode attention.
+ *
+ * For each sequence i and query head j, with L = context_lens[i],
+ * G = Hq / Hkv and kv head h = j / G:
+ *   out[i, j, :] = sum_t softmax_t(scale * <q[i,j,:], K_i[t,h,:]>) * V_i[t,h,:]
+ * over t < L, where K_i[t] / V_i[t] are read from block block_tables[i][t / B],
+ * slot t % B ([P1] sections 2 and 2.2: decode attends over every cached token
+ * of the sequence, gathered from its scattered blocks; section 2.3 item 3:
+ * ragged lengths).  L == 0 gives zeros.  No causal, sliding or bias mask.
+ *
+ *   out            device, [num_seqs, Hq, D], dtype of the cache, 16-B aligned
+ *   q              device, [num_seqs, Hq, D], dtype of the cache, 16-B aligned
+ *   block_tables   device, [num_seqs, max_blocks_per_seq] int32; only columns
+ *                  < ceil(L / B) are read (others may hold anything)
+ *   context_lens   device, [num_seqs] int32; values are clamped to
+ *                  [0, max_blocks_per_seq * B]
+ *   num_units      number of work units the tiles of the batch are split into
+ *                  (each unit is one wavefront); 0 = a default sized to the GPU.
+ *                  The split decides the order of floating-point reductions,
+ *                  so results are bit-reproducible for a given
+ *                  (context_lens, num_units) and independent of block IDs.
+ *   workspace      device scratch of at least pa_decode_workspace_bytes()
+ *                  bytes, 16-B aligned, owned by the caller; it holds partial
+ *                  results between the two kernels of one call, so calls that
+ *                  share a workspace must be ordered on one stream.
+ * Block IDs outside [0, N) in a column that is read are replaced by 0.
+ * Supported: bf16 with G in {1, 2, 4, 8, 16}; f32 with any G.  Outputs are
+ * rounded to the output dtype nearest-even from fp32 accumulators.
+ */
+size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
+                                 int32_t num_units);
+
+/* The num_units the library uses for num_units == 0 on the current device. */
+int32_t pa_decode_default_units(void);
+
+pa_status pa_paged_attn_decode(const pa_cache_desc* desc, void* out, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_q_heads,
+                               int32_t max_blocks_per_seq, float scale, int32_t num_units,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two kernels of pa_paged_attn_decode as separate calls, same arguments:
+ * _partial runs the block-table gather and attention over every work unit,
+ * writing finished sequences to `out` and partial (max, sum, accumulator)
+ * records of split sequences to the workspace; _merge then combines the
+ * partial records of each split sequence with the log-sum-exp rule.  Calling
+ * _partial then _merge on one stream with identical arguments is exactly
+ * pa_paged_attn_decode; it lets a caller time or overlap the two stages.
+ */
+pa_status pa_paged_attn_decode_partial(const pa_cache_desc* desc, void* out, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t max_blocks_per_seq, float scale,
+                                       int32_t num_units, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+pa_status pa_paged_attn_decode_merge(const pa_cache_desc* desc, void* out, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_blocks_per_seq, float scale, int32_t num_units,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host block allocator ("block manager", [P1] section 2.2; sample structure in
+ * [P3] section 2.2).  Host memory only; not thread-safe; one instance per
+ * cache.  Semantics:
+ *   - free blocks form a FIFO queue, initialised from initial_free_order
+ *     (a permutation of 0..N-1) or 0..N-1 when it is NULL;
+ *   - add(seq, n): a new sequence holds ceil(n / B) blocks taken from the head
+ *     of the queue ([P2] PagedAttention 的思路: 500 tokens -> 32 pages);
+ *     all-or-nothing: PA_ERR_OOM leaves the state unchanged;
+ *   - append(seq): reserve the slot of the next token; a new block is taken
+ *     only when the token falls past the last block ([P2] 工作原理 > 2.
+ *     按需分配); when the target block is held by more than one sequence the
+ *     writer moves to a fresh block and (cow_src, cow_dst) name the block
+ *     copy the caller must do first (copy-on-write); otherwise -1, -1;
+ *   - fork(parent, child): child shares all of parent's blocks ([P2]
+ *     优势 > 3. 支持共享: parallel sampling and beam search);
+ *   - free(seq): drop one reference per block in logical order; blocks that
+ *     reach zero join the tail of the queue ([P2] 工作原理 > 3. 及时释放).
+ * Sequence IDs are arbitrary int64 values.  PA_ERR_STATE: unknown seq, a seq
+ * that already exists (add, fork child).  State is unchanged by any error.
+ */
+typedef struct pa_allocator pa_allocator;
+
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
+                          const int32_t* initial_free_order, pa_allocator** out);
+void      pa_alloc_destroy(pa_allocator* a);
+int32_t   pa_alloc_num_free(const pa_allocator* a);                       /* -1 if a == NULL */
+int32_t   pa_alloc_num_seqs(const pa_allocator* a);                       /* -1 if a == NULL */
+int32_t   pa_alloc_refcount(const pa_allocator* a, int32_t block);        /* -1 if out of range */
+/* Copy the free queue, head first, into out[0..cap); *n = its full length. */
+pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n);
+
+pa_status pa_seq_add(pa_allocator* a, int64_t seq, int32_t num_tokens);
+pa_status pa_seq_append(pa_allocator* a, int64_t seq, int64_t* slot,
+                        int32_t* cow_src, int32_t* cow_dst);
+/*
+ * Append one token to each of seqs[0..n) in order.  slots[k] and
+ * cow_pairs[2k], cow_pairs[2k+1] receive the k-th result (-1, -1 when no
+ * copy is needed); new_blocks[k] is the block newly placed in the k-th
+ * sequence's table (a fresh page or a copy-on-write target), else -1, and
+ * new_cols[k] its table column.  Stops at the first failure:
+ * *num_done = appends completed (earlier ones stay applied), and the status
+ * is that of the failing append (PA_ERR_OOM / PA_ERR_STATE).
+ */
+pa_status pa_seq_append_batch(pa_allocator* a, const int64_t* seqs, int32_t n, int64_t* slots,
+                              int32_t* cow_pairs, int32_t* new_blocks, int32_t* new_cols,
+                              int32_t* num_done);
+pa_status pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child);
+pa_status pa_seq_free(pa_allocator* a, int64_t seq);
+/* Slots of positions start .. start+count-1 (must lie inside the sequence). */
+pa_status pa_seq_slots(const pa_allocator* a, int64_t seq, int32_t start, int32_t count,
+                       int64_t* out);
+pa_status pa_seq_info(const pa_allocator* a, int64_t seq, int32_t* num_tokens,
+                      int32_t* num_blocks);
+/* Copy the block table (logical order) into out[0..cap); PA_ERR_INVALID_ARG if cap is short. */
+pa_status pa_seq_block_table(const pa_allocator* a, int64_t seq, int32_t* out, int32_t cap);
+/*
+ * Decode metadata for seqs[0..n): block_tables [n][max_blocks_per_seq]
+ * (unused columns set to -1) and context_lens [n] (host arrays).
+ * PA_ERR_INVALID_ARG if a table is longer than max_blocks_per_seq.
+ */
+pa_status pa_batch_metadata(const pa_allocator* a, const int64_t* seqs, int32_t n,
+                            int32_t max_blocks_per_seq, int32_t* block_tables,
+                            int32_t* context_lens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,126 @@
+"""Python handle on the library's host block allocator (pa_alloc_* / pa_seq_*)."""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _native as N
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class BlockAllocator:
+    """FIFO free list, per-sequence block tables, reference counts, fork and
+    copy-on-write; every call runs in libpagedkv's C++ allocator."""
+
+    def __init__(self, num_blocks: int, block_size: int, initial_free_order=None):
+        self._lib = N.lib()
+        h = ctypes.c_void_p()
+        order = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise ValueError("initial_free_order must have num_blocks entries")
+        N.check(self._lib.pa_alloc_create(num_blocks, block_size,
+                                          None if order is None else _ptr(order),
+                                          ctypes.byref(h)), "pa_alloc_create")
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            self._lib.pa_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- queries --------------------------------------------------------------
+    def num_free(self) -> int:
+        return int(self._lib.pa_alloc_num_free(self._h))
+
+    def num_seqs(self) -> int:
+        return int(self._lib.pa_alloc_num_seqs(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_alloc_refcount(self._h, block))
+
+    def free_list(self) -> list[int]:
+        n = ctypes.c_int32()
+        N.check(self._lib.pa_alloc_free_list(self._h, None, 0, ctypes.byref(n)), "free_list")
+        out = np.empty(n.value, dtype=np.int32)
+        N.check(self._lib.pa_alloc_free_list(self._h, _ptr(out), n.value, ctypes.byref(n)),
+                "free_list")
+        return out.tolist()
+
+    def info(self, seq: int):
+        nt, nb = ctypes.c_int32(), ctypes.c_int32()
+        N.check(self._lib.pa_seq_info(self._h, seq, ctypes.byref(nt), ctypes.byref(nb)), "seq_info")
+        return nt.value, nb.value
+
+    def length(self, seq: int) -> int:
+        return self.info(seq)[0]
+
+    def block_table(self, seq: int) -> list[int]:
+        _, nb = self.info(seq)
+        out = np.empty(max(nb, 1), dtype=np.int32)
+        N.check(self._lib.pa_seq_block_table(self._h, seq, _ptr(out), nb), "seq_block_table")
+        return out[:nb].tolist()
+
+    def slots(self, seq: int, start: int, count: int) -> np.ndarray:
+        out = np.empty(max(count, 1), dtype=np.int64)
+        N.check(self._lib.pa_seq_slots(self._h, seq, start, count, _ptr(out)), "seq_slots")
+        return out[:count]
+
+    def batch_metadata(self, seqs, max_blocks_per_seq: int):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = seqs.shape[0]
+        tables = np.empty((n, max_blocks_per_seq), dtype=np.int32)
+        ctx = np.empty(n, dtype=np.int32)
+        N.check(self._lib.pa_batch_metadata(self._h, _ptr(seqs), n, max_blocks_per_seq,
+                                            _ptr(tables), _ptr(ctx)), "batch_metadata")
+        return tables, ctx
+
+    # -- operations -----------------------------------------------------------
+    def add(self, seq: int, num_tokens: int) -> None:
+        N.check(self._lib.pa_seq_add(self._h, seq, num_tokens), "seq_add")
+
+    def append(self, seq: int):
+        """Returns (slot, cow) with cow None or the (src, dst) block copy to do first."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        N.check(self._lib.pa_seq_append(self._h, seq, ctypes.byref(slot), ctypes.byref(src),
+                                        ctypes.byref(dst)), "seq_append")
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def append_batch(self, seqs):
+        """Append one token to each sequence in order.
+
+        Returns (status, done, slots[n], cow_pairs[n, 2], new_blocks[n], new_cols[n]);
+        entries past `done` are unspecified.  status is PA_OK, PA_ERR_OOM or PA_ERR_STATE.
+        """
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = seqs.shape[0]
+        slots = np.empty(n, dtype=np.int64)
+        cows = np.empty((n, 2), dtype=np.int32)
+        nb = np.empty(n, dtype=np.int32)
+        nc = np.empty(n, dtype=np.int32)
+        done = ctypes.c_int32()
+        st = self._lib.pa_seq_append_batch(self._h, _ptr(seqs), n, _ptr(slots), _ptr(cows),
+                                           _ptr(nb), _ptr(nc), ctypes.byref(done))
+        if st not in (N.PA_OK, N.PA_ERR_OOM, N.PA_ERR_STATE):
+            N.check(st, "seq_append_batch")
+        return st, done.value, slots, cows, nb, nc
+
+    def fork(self, parent: int, child: int) -> None:
+        N.check(self._lib.pa_seq_fork(self._h, parent, child), "seq_fork")
+
+    def free(self, seq: int) -> None:
+        N.check(self._lib.pa_seq_free(self._h, seq), "seq_free")

@@ -1,0 +1,249 @@
+// C ABI of libpagedkv: argument validation and kernel launches.  The kernels
+// live in kernels_cache.hip and kernels_decode.hip; the host allocator in
+// allocator.cpp.  No entry point allocates device memory.
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "pagedkv.h"
+#include "pagedkv_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Checks a descriptor: INVALID_ARG for impossible values, UNSUPPORTED for
+// valid ones this build has no kernels for.
+pa_status check_desc(const pa_cache_desc* d) {
+    if (!d) return PA_ERR_INVALID_ARG;
+    if (d->num_blocks <= 0 || d->block_size <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
+    if (d->block_size != 16 && d->block_size != 32 && d->block_size != 64) return PA_ERR_UNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+size_t elem_bytes(const pa_cache_desc* d) { return d->dtype == PA_DTYPE_F32 ? 4 : 2; }
+
+pa_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return PA_OK;
+    if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
+    return PA_ERR_HIP;
+}
+
+bool group_kernel_for(const pa_cache_desc* d, int32_t group) {
+    return d->dtype == PA_DTYPE_BF16 && group > 1;
+}
+
+// Partial-result floats per piece and bytes of the workspace for W units.
+size_t workspace_for(const pa_cache_desc* d, int32_t num_q_heads, int32_t units) {
+    const int32_t group = num_q_heads / d->num_kv_heads;
+    const int32_t gh = group_kernel_for(d, group) ? group : 1;
+    const size_t pf = static_cast<size_t>(gh) * d->head_dim + ((2 * gh + 3) & ~3);
+    const size_t pieces = static_cast<size_t>(units) * 2 * pf * sizeof(float);
+    const size_t recs = static_cast<size_t>(units) * pkv::kRecInts * sizeof(int32_t);
+    return ((pieces + 255) & ~size_t(255)) + recs;
+}
+
+std::atomic<int32_t> g_default_units{0};
+
+constexpr int32_t kMaxUnits = 1 << 20;
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+    switch (s) {
+        case PA_OK: return "ok";
+        case PA_ERR_INVALID_ARG: return "invalid argument";
+        case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case PA_ERR_OOM: return "out of free blocks";
+        case PA_ERR_STATE: return "unknown, duplicate or already-freed sequence";
+        case PA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t pa_abi_version(void) { return (1 << 16) | 0; }
+
+size_t pa_cache_bytes(const pa_cache_desc* d) {
+    if (check_desc(d) != PA_OK) return 0;
+    return static_cast<size_t>(d->num_blocks) * d->num_kv_heads * d->block_size * d->head_dim *
+           elem_bytes(d);
+}
+
+pa_status pa_reshape_and_cache(const pa_cache_desc* d, const void* k, const void* v,
+                               const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                               void* v_cache, void* stream) {
+    pa_status st = check_desc(d);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(slot_mapping, 8))
+        return PA_ERR_INVALID_ARG;
+    if (d->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+    return from_hip(pkv::launch_reshape_and_cache(d->dtype, d->head_dim, d->block_size,
+                                                  d->num_kv_heads, d->num_blocks, k, v,
+                                                  slot_mapping, num_tokens, k_cache, v_cache,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks(const pa_cache_desc* d, void* k_cache, void* v_cache,
+                         const int32_t* pairs, int32_t num_pairs, void* stream) {
+    pa_status st = check_desc(d);
+    if (st != PA_OK) return st;
+    if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !pairs) return PA_ERR_INVALID_ARG;
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pairs, 4))
+        return PA_ERR_INVALID_ARG;
+    return from_hip(pkv::launch_copy_blocks(d->dtype, d->head_dim, d->block_size, d->num_kv_heads,
+                                            d->num_blocks, k_cache, v_cache, pairs, num_pairs,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_update_block_tables(int32_t* block_tables, int32_t num_rows,
+                                 int32_t max_blocks_per_seq, const int32_t* updates,
+                                 int32_t num_updates, void* stream) {
+    if (num_rows < 0 || max_blocks_per_seq < 0 || num_updates < 0) return PA_ERR_INVALID_ARG;
+    if (num_updates == 0) return PA_OK;
+    if (!block_tables || !updates || !aligned(block_tables, 4) || !aligned(updates, 4))
+        return PA_ERR_INVALID_ARG;
+    return from_hip(pkv::launch_update_block_tables(block_tables, num_rows, max_blocks_per_seq,
+                                                    updates, num_updates,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_default_units(void) {
+    int32_t u = g_default_units.load();
+    if (u > 0) return u;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    u = cus * 8;
+    g_default_units.store(u);
+    return u;
+}
+
+size_t pa_decode_workspace_bytes(const pa_cache_desc* d, int32_t num_q_heads, int32_t num_units) {
+    if (check_desc(d) != PA_OK || num_q_heads <= 0 || num_q_heads % d->num_kv_heads != 0 ||
+        num_units < 0 || num_units > kMaxUnits)
+        return 0;
+    const int32_t units = num_units == 0 ? pa_decode_default_units() : num_units;
+    return workspace_for(d, num_q_heads, units);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation and argument packing shared by the three decode entry points.
+pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_blocks_per_seq, float scale, int32_t num_units, void* workspace,
+                      size_t workspace_bytes, void* stream, int passes) {
+    pa_status st = check_desc(d);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || num_units < 0 ||
+        num_units > kMaxUnits)
+        return PA_ERR_INVALID_ARG;
+    if (num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+    const int32_t group = num_q_heads / d->num_kv_heads;
+    const bool use_group = group_kernel_for(d, group);
+    if (use_group && group != 2 && group != 4 && group != 8 && group != 16)
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    if (max_blocks_per_seq == 0) return PA_ERR_INVALID_ARG;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(workspace, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return PA_ERR_INVALID_ARG;
+    const int32_t units = num_units == 0 ? pa_decode_default_units() : num_units;
+    if (workspace_bytes < workspace_for(d, num_q_heads, units)) return PA_ERR_INVALID_ARG;
+    const int32_t tpb = d->block_size / pkv::kTile;
+    const int32_t rows = use_group ? d->num_kv_heads : num_q_heads;
+    // Every tile position of the batch (rows x sequences x table columns) must fit in int32.
+    const double positions = static_cast<double>(rows) * num_seqs * max_blocks_per_seq * tpb;
+    if (positions + units >= 2147483647.0) return PA_ERR_UNSUPPORTED;
+
+    pkv::DecodeArgs a;
+    a.q = q;
+    a.out = out;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.pieces = static_cast<float*>(workspace);
+    {
+        const int32_t gh = use_group ? group : 1;
+        const size_t pf = static_cast<size_t>(gh) * d->head_dim + ((2 * gh + 3) & ~3);
+        const size_t pieces = static_cast<size_t>(units) * 2 * pf * sizeof(float);
+        a.unit_rec = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                ((pieces + 255) & ~size_t(255)));
+        a.heads_per_row = gh;
+    }
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = d->num_kv_heads;
+    a.group = group;
+    a.rows = rows;
+    a.max_blocks = max_blocks_per_seq;
+    a.tiles_per_block = tpb;
+    a.num_blocks = d->num_blocks;
+    a.num_units = units;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    return from_hip(pkv::launch_decode(d->dtype, d->head_dim, use_group, a, passes,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_paged_attn_decode(const pa_cache_desc* d, void* out, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_q_heads,
+                               int32_t max_blocks_per_seq, float scale, int32_t num_units,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                       num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
+                       workspace_bytes, stream, 3);
+}
+
+pa_status pa_paged_attn_decode_partial(const pa_cache_desc* d, void* out, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t max_blocks_per_seq, float scale,
+                                       int32_t num_units, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                       num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
+                       workspace_bytes, stream, 1);
+}
+
+pa_status pa_paged_attn_decode_merge(const pa_cache_desc* d, void* out, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_blocks_per_seq, float scale, int32_t num_units,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                       num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
+                       workspace_bytes, stream, 2);
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Cache-side kernels: scatter of new tokens into their slots, whole-block copy,
+// and in-place block-table updates.  All three are pure data movement (bits in,
+// bits out); the physical layout they write is the one declared in pagedkv.h.
+
+#include "pagedkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// One workgroup per (token, kv head); one thread per head-dim position.
+// Writing new tokens into the slots of their blocks is the "scatter" half of
+// paged KV access (ksqn.cn "大模型推理性能优化：PagedAttention与Continuous
+// Batching原理与实践", section 2.2).  Thread d stores V element d; threads with
+// d % X == 0 also copy the 16-byte K group of dims d .. d+X-1.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void reshape_and_cache_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const int64_t* __restrict__ slots,
+    T* __restrict__ k_cache, T* __restrict__ v_cache, int num_kv_heads, int block_size,
+    int64_t num_slots) {
+    constexpr int X = 16 / sizeof(T);  // elements per 16-byte group
+    constexpr int E = X / 4;           // dims per 16-byte V group
+    const int t = blockIdx.x;
+    const int h = blockIdx.y;
+    const int d = threadIdx.x;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) return;
+    const int64_t b = slot / block_size;
+    const int o = static_cast<int>(slot - b * block_size);
+    const int tpb = block_size / kTile;
+    const size_t tile_base =
+        ((static_cast<size_t>(b) * num_kv_heads + h) * tpb + (o >> 4)) * (kTile * D);
+    const size_t src = (static_cast<size_t>(t) * num_kv_heads + h) * D;
+    const int ti = o & 15;
+    // V: 16-byte group (m, j, i) holds tokens 4j..4j+3 of dims 16E*m + 16e + i.
+    const int m = d / (16 * E);
+    const int e = (d >> 4) % E;
+    const int i = d & 15;
+    const int j = ti >> 2;
+    const int r = ti & 3;
+    v_cache[tile_base + ((((m * 4 + j) * 16 + i) * E + e) * 4 + r)] = v[src + d];
+    // K: 16-byte group (c, token) holds dims c*X .. c*X+X-1 of one token.
+    if (d % X == 0) {
+        const int c = d / X;
+        *reinterpret_cast<u32x4*>(k_cache + tile_base + (c * 16 + ti) * X) =
+            *reinterpret_cast<const u32x4*>(k + src + d);
+    }
+}
+
+// Grid (pairs, 2 arrays, chunks); 256 threads copy 16 bytes each per chunk.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_cache,
+                                                          u32x4* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int num_blocks, int64_t block_u4) {
+    const int src = pairs[2 * blockIdx.x];
+    const int dst = pairs[2 * blockIdx.x + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+    u32x4* base = blockIdx.y == 0 ? k_cache : v_cache;
+    const int64_t n = static_cast<int64_t>(blockIdx.z) * 1024 + threadIdx.x;
+    const u32x4* s = base + src * block_u4;
+    u32x4* dp = base + dst * block_u4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t idx = n + k * 256;
+        if (idx < block_u4) dp[idx] = s[idx];
+    }
+}
+
+__global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict__ tables, int rows,
+                                                            int cols,
+                                                            const int32_t* __restrict__ upd,
+                                                            int n) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= n) return;
+    const int r = upd[3 * k];
+    const int c = upd[3 * k + 1];
+    if (r < 0 || r >= rows || c < 0 || c >= cols) return;
+    tables[static_cast<int64_t>(r) * cols + c] = upd[3 * k + 2];
+}
+
+template <typename T, int D>
+hipError_t launch_rc(const void* k, const void* v, const int64_t* slots, int num_tokens,
+                     void* kc, void* vc, int hkv, int bs, int nb, hipStream_t st) {
+    dim3 grid(num_tokens, hkv);
+    hipLaunchKernelGGL((reshape_and_cache_kernel<T, D>), grid, dim3(D), 0, st,
+                       static_cast<const T*>(k), static_cast<const T*>(v), slots,
+                       static_cast<T*>(kc), static_cast<T*>(vc), hkv, bs,
+                       static_cast<int64_t>(nb) * bs);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(int dtype, int head_dim, int block_size, int num_kv_heads,
+                                    int num_blocks, const void* k, const void* v,
+                                    const int64_t* slots, int num_tokens, void* k_cache,
+                                    void* v_cache, hipStream_t stream) {
+    const bool f32 = dtype == 0;
+    if (head_dim == 64)
+        return f32 ? launch_rc<uint32_t, 64>(k, v, slots, num_tokens, k_cache, v_cache,
+                                             num_kv_heads, block_size, num_blocks, stream)
+                   : launch_rc<uint16_t, 64>(k, v, slots, num_tokens, k_cache, v_cache,
+                                             num_kv_heads, block_size, num_blocks, stream);
+    if (head_dim == 128)
+        return f32 ? launch_rc<uint32_t, 128>(k, v, slots, num_tokens, k_cache, v_cache,
+                                              num_kv_heads, block_size, num_blocks, stream)
+                   : launch_rc<uint16_t, 128>(k, v, slots, num_tokens, k_cache, v_cache,
+                                              num_kv_heads, block_size, num_blocks, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy_blocks(int dtype, int head_dim, int block_size, int num_kv_heads,
+                              int num_blocks, void* k_cache, void* v_cache, const int32_t* pairs,
+                              int num_pairs, hipStream_t stream) {
+    const int64_t elem = dtype == 0 ? 4 : 2;
+    const int64_t block_u4 = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem / 16;
+    const int64_t chunks = (block_u4 + 1023) / 1024;
+    dim3 grid(num_pairs, 2, static_cast<unsigned>(chunks));
+    hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream,
+                       static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), pairs,
+                       num_blocks, block_u4);
+    return hipGetLastError();
+}
+
+hipError_t launch_update_block_tables(int32_t* tables, int rows, int cols, const int32_t* upd,
+                                      int n, hipStream_t stream) {
+    hipLaunchKernelGGL(update_tables_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, tables,
+                       rows, cols, upd, n);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,57 @@
+// Internal declarations shared by the launchers and the kernels of libpagedkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kTile = 16;  // tokens per tile (a block holds block_size / 16 tiles)
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// Everything pass 1 and pass 2 of decode need; passed by value to both kernels.
+struct DecodeArgs {
+    const void* q;              // [S, Hq, D]
+    void* out;                  // [S, Hq, D]
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;  // [S, max_blocks]
+    const int32_t* context_lens;  // [S]
+    float* pieces;              // [units][2][piece_floats]
+    int32_t* unit_rec;          // [units][kRecInts]
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;              // Hq / Hkv
+    int32_t rows;               // work rows: Hkv (group kernel) or Hq (per-head kernel)
+    int32_t heads_per_row;      // G (group kernel) or 1 (per-head kernel)
+    int32_t max_blocks;
+    int32_t tiles_per_block;
+    int32_t num_blocks;
+    int32_t num_units;
+    float scale_log2e;          // scale * log2(e): scores are kept in base-2 units
+};
+
+constexpr int kRecInts = 8;  // per-unit record: row, seq, seq_begin, seq_end, tiles_per_unit
+
+// Floats of one partial-result record: heads_per_row * (D accumulators + max + sum).
+inline size_t piece_floats(int heads_per_row, int head_dim) {
+    return static_cast<size_t>(heads_per_row) * (head_dim + 2);
+}
+
+hipError_t launch_reshape_and_cache(int dtype, int head_dim, int block_size, int num_kv_heads,
+                                    int num_blocks, const void* k, const void* v,
+                                    const int64_t* slots, int num_tokens, void* k_cache,
+                                    void* v_cache, hipStream_t stream);
+hipError_t launch_copy_blocks(int dtype, int head_dim, int block_size, int num_kv_heads,
+                              int num_blocks, void* k_cache, void* v_cache, const int32_t* pairs,
+                              int num_pairs, hipStream_t stream);
+hipError_t launch_update_block_tables(int32_t* tables, int rows, int cols, const int32_t* upd,
+                                      int n, hipStream_t stream);
+// passes: bit 0 = pass 1 (tiles -> outputs / partial records), bit 1 = pass 2 (merge).
+// Returns hipErrorInvalidValue for an uncompiled (dtype, head_dim, group) combination.
+hipError_t launch_decode(int dtype, int head_dim, bool use_group_kernel, const DecodeArgs& a,
+                         int passes, hipStream_t stream);
+
+}  // namespace pkv

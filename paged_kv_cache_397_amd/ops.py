@@ -1,0 +1,166 @@
+"""Device ops: thin wrappers that pass torch tensors' device pointers and the
+current HIP stream to libpagedkv.  Every computation runs in the library's HIP
+kernels; these functions only check shapes/dtypes and marshal arguments.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _native as N
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+_PA_DTYPE = {"f32": 0, "bf16": 1}
+
+
+@dataclass(frozen=True)
+class CacheSpec:
+    """Shape of one paged KV cache (see the layout contract in include/pagedkv.h)."""
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str  # "bf16" | "f32"
+
+    def desc(self) -> N.CacheDesc:
+        return N.CacheDesc(self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim,
+                           _PA_DTYPE[self.dtype])
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPE[self.dtype]
+
+    @property
+    def elems(self) -> int:
+        return self.num_blocks * self.num_kv_heads * self.block_size * self.head_dim
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def cache_bytes(spec: CacheSpec) -> int:
+    return int(N.lib().pa_cache_bytes(ctypes.byref(spec.desc())))
+
+
+def empty_cache(spec: CacheSpec, device="cuda"):
+    """Uninitialised K and V cache arrays (flat, spec.elems elements each)."""
+    k = torch.empty(spec.elems, dtype=spec.torch_dtype, device=device)
+    v = torch.empty(spec.elems, dtype=spec.torch_dtype, device=device)
+    return k, v
+
+
+def reshape_and_cache(spec: CacheSpec, k, v, slot_mapping, k_cache, v_cache, stream=None):
+    """Write k[t], v[t] ([T, Hkv, D]) into slot slot_mapping[t] (int64, -1 = skip)."""
+    T = slot_mapping.numel()
+    if tuple(k.shape) != (T, spec.num_kv_heads, spec.head_dim) or k.shape != v.shape:
+        raise ValueError("k and v must be [T, Hkv, D]")
+    st = N.lib().pa_reshape_and_cache(
+        ctypes.byref(spec.desc()), _dev(k, "k", spec.torch_dtype), _dev(v, "v", spec.torch_dtype),
+        _dev(slot_mapping, "slot_mapping", torch.int64), T,
+        _dev(k_cache, "k_cache", spec.torch_dtype), _dev(v_cache, "v_cache", spec.torch_dtype),
+        _stream(stream))
+    N.check(st, "pa_reshape_and_cache")
+
+
+def copy_blocks(spec: CacheSpec, k_cache, v_cache, pairs, stream=None):
+    """Copy block src onto dst for each row (src, dst) of pairs ([n, 2] int32)."""
+    n = pairs.shape[0] if pairs.dim() == 2 else pairs.numel() // 2
+    st = N.lib().pa_copy_blocks(
+        ctypes.byref(spec.desc()), _dev(k_cache, "k_cache", spec.torch_dtype),
+        _dev(v_cache, "v_cache", spec.torch_dtype), _dev(pairs, "pairs", torch.int32), n,
+        _stream(stream))
+    N.check(st, "pa_copy_blocks")
+
+
+def update_block_tables(block_tables, updates, stream=None):
+    """Apply (row, column, block) rows of updates ([n, 3] int32) to block_tables."""
+    rows, cols = block_tables.shape
+    n = updates.shape[0] if updates.dim() == 2 else updates.numel() // 3
+    st = N.lib().pa_update_block_tables(
+        _dev(block_tables, "block_tables", torch.int32), rows, cols,
+        _dev(updates, "updates", torch.int32), n, _stream(stream))
+    N.check(st, "pa_update_block_tables")
+
+
+def default_units() -> int:
+    return int(N.lib().pa_decode_default_units())
+
+
+def decode_workspace_bytes(spec: CacheSpec, num_q_heads: int, num_units: int = 0) -> int:
+    n = int(N.lib().pa_decode_workspace_bytes(ctypes.byref(spec.desc()), num_q_heads, num_units))
+    if n == 0:
+        raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "pa_decode_workspace_bytes")
+    return n
+
+
+def decode_workspace(spec: CacheSpec, num_q_heads: int, num_units: int = 0, device="cuda"):
+    return torch.empty(decode_workspace_bytes(spec, num_q_heads, num_units), dtype=torch.uint8,
+                       device=device)
+
+
+def _decode(fn: str, spec: CacheSpec, out, q, k_cache, v_cache, block_tables, context_lens,
+            scale, num_units, workspace, stream):
+    S, Hq, D = q.shape
+    if D != spec.head_dim or tuple(out.shape) != (S, Hq, D):
+        raise ValueError("q and out must be [S, Hq, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [S, maxB] and context_lens [S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = decode_workspace(spec, Hq, num_units, q.device)
+    st = getattr(N.lib(), fn)(
+        ctypes.byref(spec.desc()), _dev(out, "out", spec.torch_dtype),
+        _dev(q, "q", spec.torch_dtype), _dev(k_cache, "k_cache", spec.torch_dtype),
+        _dev(v_cache, "v_cache", spec.torch_dtype),
+        _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, block_tables.shape[1],
+        float(scale), int(num_units), _dev(workspace, "workspace"), workspace.numel(),
+        _stream(stream))
+    N.check(st, fn)
+    return out
+
+
+def paged_attn_decode(spec: CacheSpec, out, q, k_cache, v_cache, block_tables, context_lens,
+                      scale: float | None = None, num_units: int = 0, workspace=None,
+                      stream=None):
+    """out[i, j] = softmax attention of q[i, j] over sequence i's cached tokens."""
+    return _decode("pa_paged_attn_decode", spec, out, q, k_cache, v_cache, block_tables,
+                   context_lens, scale, num_units, workspace, stream)
+
+
+def paged_attn_decode_partial(spec: CacheSpec, out, q, k_cache, v_cache, block_tables,
+                              context_lens, scale: float | None = None, num_units: int = 0,
+                              workspace=None, stream=None):
+    """First kernel of paged_attn_decode (needs the same workspace in the merge)."""
+    if workspace is None:
+        raise ValueError("the partial/merge split needs an explicit shared workspace")
+    return _decode("pa_paged_attn_decode_partial", spec, out, q, k_cache, v_cache, block_tables,
+                   context_lens, scale, num_units, workspace, stream)
+
+
+def paged_attn_decode_merge(spec: CacheSpec, out, q, k_cache, v_cache, block_tables,
+                            context_lens, scale: float | None = None, num_units: int = 0,
+                            workspace=None, stream=None):
+    """Second kernel of paged_attn_decode: merges the partial records of split sequences."""
+    if workspace is None:
+        raise ValueError("the partial/merge split needs an explicit shared workspace")
+    return _decode("pa_paged_attn_decode_merge", spec, out, q, k_cache, v_cache, block_tables,
+                   context_lens, scale, num_units, workspace, stream)

@@ -30,9 +30,9 @@ def stream(seed: int, *tags: int) -> np.random.Generator:
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     """Round finite float32 values to bfloat16, nearest-even; return uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    u = x.view(np.uint32)
+    # finite inputs stay below 0xFF800000, so the sum cannot wrap in 32 bits
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
 
 
