@@ -45,6 +45,11 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Reinterpret one 32-bit word as two bf16.  The word is taken by value on purpose:
+// clang's __builtin_bit_cast applied directly to an ext-vector element reads
+// element 0 whatever the index, so vector elements must be copied out first.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -141,9 +146,8 @@ struct HeadPath {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 if constexpr (kBf16) {
-                    part = __builtin_amdgcn_fdot2_f32_bf16(
-                        __builtin_bit_cast(bf16x2, kb[s][w]), __builtin_bit_cast(bf16x2, st.q[s][w]),
-                        part, false);
+                    part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kb[s][w]),
+                                                           as_bf16x2(st.q[s][w]), part, false);
                 } else {
                     part = __builtin_fmaf(__uint_as_float(kb[s][w]), __uint_as_float(st.q[s][w]),
                                           part);
