@@ -44,7 +44,54 @@ def parse():
     ap.add_argument("--units", type=int, default=0, help="decode work units (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, copy a MIB-MiB device buffer 5 times (a plain "
+                         "copy of known size, used to scale hardware byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """Device-to-device copies of a known size: the reference for FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    t = min(times)
+    print(json.dumps({"copy_calibration_bytes": n, "reads_bytes": n, "writes_bytes": n,
+                      "best_us": round(t * 1e6, 2),
+                      "read_plus_write_gbps": round(2 * n / t / 1e9, 1)}), flush=True)
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_397_amd", "csrc", "kernels_decode.hip")
+
+
+def measured_traffic(config_name: str):
+    """HBM bytes per launch of the decode kernel from the committed counter summary
+    (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or
+    None when there is none for this workload or the kernel source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_{config_name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            fields[k.strip()] = v.strip()
+    digest = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, ctx, q_host, seconds):
@@ -103,6 +150,9 @@ def main():
               f"shards by sequence or KV head with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     from paged_kv_cache_397_amd import ops, _native
     from paged_kv_cache_397_amd.batch import PagedKVCache, to_device
@@ -221,7 +271,7 @@ def main():
             ops.update_block_tables(tables, du[:len(upd_rows)])
         # a4: cache write of the step's new tokens
         ops.reshape_and_cache(spec, ks[n], vs[n], ds, cache.k, cache.v)
-        # a5-a11: decode attention, pass 1 then the merge
+        # a5-a11: decode attention, pass 1 (gather + attention) then pass 2 (merge)
         if timed:
             e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             e1.record(stream)
@@ -282,7 +332,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(p1_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name),
             "pass1_us_mean": round(float(t_p1.mean()) * 1e6, 2),
             "pass1_us_median": round(float(np.median(t_p1)) * 1e6, 2),
             "algorithmic_bytes_per_launch": int(np.median(kv_bytes)),

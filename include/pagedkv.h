@@ -150,9 +150,10 @@ pa_status pa_update_block_tables(int32_t* block_tables, int32_t num_rows,
  *                  so results are bit-reproducible for a given
  *                  (context_lens, num_units) and independent of block IDs.
  *   workspace      device scratch of at least pa_decode_workspace_bytes()
- *                  bytes, 16-B aligned, owned by the caller; it holds partial
- *                  results between the two kernels of one call, so calls that
- *                  share a workspace must be ordered on one stream.
+ *                  bytes, 16-B aligned, owned by the caller (no initial contents
+ *                  needed); it holds partial results between the two kernels
+ *                  of one call, so calls that share a workspace must be ordered
+ *                  on one stream.
  * Block IDs outside [0, N) in a column that is read are replaced by 0.
  * Supported: bf16 with G in {1, 2, 4, 8, 16}; f32 with any G.  Outputs are
  * rounded to the output dtype nearest-even from fp32 accumulators.
@@ -171,13 +172,16 @@ pa_status pa_paged_attn_decode(const pa_cache_desc* desc, void* out, const void*
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The two kernels of pa_paged_attn_decode as separate calls, same arguments:
- * _partial runs the block-table gather and attention over every work unit,
- * writing finished sequences to `out` and partial (max, sum, accumulator)
- * records of split sequences to the workspace; _merge then combines the
- * partial records of each split sequence with the log-sum-exp rule.  Calling
- * _partial then _merge on one stream with identical arguments is exactly
- * pa_paged_attn_decode; it lets a caller time or overlap the two stages.
+ * pa_paged_attn_decode enqueues two kernels.  The first gathers and attends:
+ * each wave takes an equal range of the batch's 16-token tiles, writes the
+ * sequences it holds whole to `out` and leaves partial (max, sum, accumulator)
+ * records for sequences cut by range ends.  The second merges the records of
+ * every cut sequence with the log-sum-exp rule ([P1] section 2.2 names only the
+ * gather; the split and the merge are this library's).
+ *
+ * The two kernels as separate calls, same arguments: _partial, then _merge on
+ * one stream is exactly pa_paged_attn_decode (bit-identical outputs); it lets a
+ * caller time or overlap the two stages.
  */
 pa_status pa_paged_attn_decode_partial(const pa_cache_desc* desc, void* out, const void* q,
                                        const void* k_cache, const void* v_cache,

@@ -37,14 +37,26 @@ bool group_kernel_for(const pa_cache_desc* d, int32_t group) {
     return d->dtype == PA_DTYPE_BF16 && group > 1;
 }
 
-// Partial-result floats per piece and bytes of the workspace for W units.
-size_t workspace_for(const pa_cache_desc* d, int32_t num_q_heads, int32_t units) {
+// Workspace of W units: partial records (two per unit) | unit records.
+struct WorkspaceLayout {
+    size_t piece_floats;  // floats of one partial record
+    size_t rec_offset;    // bytes to the unit records
+    size_t bytes;         // total
+};
+
+WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t num_q_heads, int32_t units) {
     const int32_t group = num_q_heads / d->num_kv_heads;
     const int32_t gh = group_kernel_for(d, group) ? group : 1;
-    const size_t pf = static_cast<size_t>(gh) * d->head_dim + ((2 * gh + 3) & ~3);
-    const size_t pieces = static_cast<size_t>(units) * 2 * pf * sizeof(float);
-    const size_t recs = static_cast<size_t>(units) * pkv::kRecInts * sizeof(int32_t);
-    return ((pieces + 255) & ~size_t(255)) + recs;
+    WorkspaceLayout w;
+    w.piece_floats = static_cast<size_t>(gh) * d->head_dim + ((2 * gh + 3) & ~3);
+    const size_t pieces = static_cast<size_t>(units) * 2 * w.piece_floats * sizeof(float);
+    w.rec_offset = (pieces + 255) & ~size_t(255);
+    w.bytes = w.rec_offset + static_cast<size_t>(units) * pkv::kRecInts * sizeof(int32_t);
+    return w;
+}
+
+size_t workspace_for(const pa_cache_desc* d, int32_t num_q_heads, int32_t units) {
+    return workspace_layout(d, num_q_heads, units).bytes;
 }
 
 std::atomic<int32_t> g_default_units{0};
@@ -129,7 +141,9 @@ int32_t pa_decode_default_units(void) {
         (void)hipGetLastError();
         cus = 256;
     }
-    u = cus * 8;
+    // Five one-wave units per CU keep about 10 MiB of K/V reads in flight at one
+    // tile per wave, the measured optimum of pass 1 on MI355X (256 CUs -> 1280).
+    u = cus * 5;
     g_default_units.store(u);
     return u;
 }
@@ -177,6 +191,9 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     // Every tile position of the batch (rows x sequences x table columns) must fit in int32.
     const double positions = static_cast<double>(rows) * num_seqs * max_blocks_per_seq * tpb;
     if (positions + units >= 2147483647.0) return PA_ERR_UNSUPPORTED;
+    // Tile indices into the cache (block * Hkv + head) * tpb + tile are int32 in the kernels.
+    if (static_cast<double>(d->num_blocks) * d->num_kv_heads * tpb >= 2147483647.0)
+        return PA_ERR_UNSUPPORTED;
 
     pkv::DecodeArgs a;
     a.q = q;
@@ -185,14 +202,12 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     a.v_cache = v_cache;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
-    a.pieces = static_cast<float*>(workspace);
     {
-        const int32_t gh = use_group ? group : 1;
-        const size_t pf = static_cast<size_t>(gh) * d->head_dim + ((2 * gh + 3) & ~3);
-        const size_t pieces = static_cast<size_t>(units) * 2 * pf * sizeof(float);
-        a.unit_rec = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                                ((pieces + 255) & ~size_t(255)));
-        a.heads_per_row = gh;
+        const WorkspaceLayout w = workspace_layout(d, num_q_heads, units);
+        char* base = static_cast<char*>(workspace);
+        a.pieces = reinterpret_cast<float*>(base);
+        a.unit_rec = reinterpret_cast<int32_t*>(base + w.rec_offset);
+        a.heads_per_row = use_group ? group : 1;
     }
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;

@@ -68,6 +68,10 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0): wait until every vector-memory load of the wave has returned
+// (expcnt and lgkmcnt fields left at their maxima, i.e. not waited on).
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -117,6 +121,14 @@ __device__ void write_zero_seq(const DecodeArgs& a, int seq, int lane) {
 }
 
 // ---------------------------------------------------------------------------------
+// A path supplies, for one work row (its query heads, its KV head):
+//   Q, Acc              query registers and running softmax state
+//   kv_head(a, row)     the KV head a row reads
+//   load_q / reset      start a piece
+//   tile                fold one 16-token tile into Acc
+//   finish              write the piece: `out` when the unit holds the whole
+//                       sequence, else a partial (acc, max, sum) record
+//
 // Per-head path (VALU).  Lane l = 16 j + i.
 //   K load s: token i, dims (4s + j) X + x       (x < X)
 //   V load m: tokens 4j .. 4j+3, dims 16E m + 16e + i   (e < E)
@@ -127,17 +139,40 @@ struct HeadPath {
     static constexpr int NL = D * static_cast<int>(sizeof(T)) / 64;  // 16-B loads per lane per tile
     static constexpr int TILE_U4 = D * static_cast<int>(sizeof(T));   // tile size in 16-B units
     static constexpr bool kBf16 = sizeof(T) == 2;
+    static constexpr int GH = 1;  // query heads per row
 
-    static __device__ int piece_floats() { return (D + 2 + 3) & ~3; }
-
-    struct State {
-        u32x4 q[NL];
+    struct Q {
+        u32x4 v[NL];
+    };
+    struct Acc {
         float m, l;
         float acc[NL][E];
     };
 
-    static __device__ __forceinline__ void tile(const DecodeArgs& a, State& st, const u32x4* kb,
-                                                const u32x4* vb, int t, int ctx, int lane) {
+    static __device__ __forceinline__ int kv_head(const DecodeArgs& a, int row) {
+        return row / a.group;
+    }
+
+    static __device__ __forceinline__ void load_q(const DecodeArgs& a, Q& q, int row, int seq,
+                                                  int lane) {
+        const int j = lane >> 4;
+        const T* qrow = static_cast<const T*>(a.q) + (static_cast<size_t>(seq) * a.num_q_heads + row) * D;
+#pragma unroll
+        for (int s = 0; s < NL; ++s) q.v[s] = *reinterpret_cast<const u32x4*>(qrow + (4 * s + j) * X);
+    }
+
+    static __device__ __forceinline__ void reset(Acc& st) {
+        st.m = kNegInf;
+        st.l = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < NL; ++mm)
+#pragma unroll
+            for (int e = 0; e < E; ++e) st.acc[mm][e] = 0.f;
+    }
+
+    static __device__ __forceinline__ void tile(const DecodeArgs& a, Acc& st, const Q& q,
+                                                const u32x4* kb, const u32x4* vb, int t, int ctx,
+                                                int lane) {
         const int j = lane >> 4, i = lane & 15;
         // QK: partial dot over this lane's dims, then across the four rows.
         float part = 0.f;
@@ -147,9 +182,9 @@ struct HeadPath {
             for (int w = 0; w < 4; ++w) {
                 if constexpr (kBf16) {
                     part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kb[s][w]),
-                                                           as_bf16x2(st.q[s][w]), part, false);
+                                                           as_bf16x2(q.v[s][w]), part, false);
                 } else {
-                    part = __builtin_fmaf(__uint_as_float(kb[s][w]), __uint_as_float(st.q[s][w]),
+                    part = __builtin_fmaf(__uint_as_float(kb[s][w]), __uint_as_float(q.v[s][w]),
                                           part);
                 }
             }
@@ -200,9 +235,8 @@ struct HeadPath {
         }
     }
 
-    template <bool kWhole>
-    static __device__ void finish(const DecodeArgs& a, State& st, int qh, int seq, float* rec,
-                                  int lane) {
+    static __device__ __forceinline__ void finish(const DecodeArgs& a, Acc& st, int row, int seq,
+                                                  bool whole, float* rec, int lane) {
         const int j = lane >> 4, i = lane & 15;
         float L = st.l;
         L += __shfl_xor(L, 1);
@@ -220,8 +254,8 @@ struct HeadPath {
             }
         }
         if (j != 0) return;
-        if constexpr (kWhole) {
-            T* o = static_cast<T*>(a.out) + (static_cast<size_t>(seq) * a.num_q_heads + qh) * D;
+        if (whole) {
+            T* o = static_cast<T*>(a.out) + (static_cast<size_t>(seq) * a.num_q_heads + row) * D;
             const float inv = 1.f / L;
 #pragma unroll
             for (int mm = 0; mm < NL; ++mm)
@@ -238,32 +272,6 @@ struct HeadPath {
             }
         }
     }
-
-    static __device__ void piece(const DecodeArgs& a, int row, int seq, int t0, int t1, bool whole,
-                                 float* rec, int lane) {
-        const int qh = row;
-        const int kvh = qh / a.group;
-        const int j = lane >> 4;
-        const int ctx = ctx_of(a, seq);
-        State st;
-        const T* qrow = static_cast<const T*>(a.q) + (static_cast<size_t>(seq) * a.num_q_heads + qh) * D;
-#pragma unroll
-        for (int s = 0; s < NL; ++s) st.q[s] = *reinterpret_cast<const u32x4*>(qrow + (4 * s + j) * X);
-        st.m = kNegInf;
-        st.l = 0.f;
-#pragma unroll
-        for (int mm = 0; mm < NL; ++mm)
-#pragma unroll
-            for (int e = 0; e < E; ++e) st.acc[mm][e] = 0.f;
-        run_tiles(a, st, seq, kvh, t0, t1, ctx, lane);
-        if (whole)
-            finish<true>(a, st, qh, seq, rec, lane);
-        else
-            finish<false>(a, st, qh, seq, rec, lane);
-    }
-
-    static __device__ void run_tiles(const DecodeArgs& a, State& st, int seq, int kvh, int t0,
-                                     int t1, int ctx, int lane);
 };
 
 // ---------------------------------------------------------------------------------
@@ -273,27 +281,49 @@ struct HeadPath {
 //   V load m: tokens 4j .. 4j+3 of dims 32 m + i (words 0,1) and 32 m + 16 + i (words 2,3)
 //             -> A operands of the two 16-dim groups 2m, 2m+1
 //   acc[g][r]: dim 16 g + 4 j + r, head column i
-template <int D>
+template <int D, int G>
 struct GroupPath {
     using T = uint16_t;
+    static constexpr int GH = G;  // query heads per row
     static constexpr int NL = D / 32;  // 16-B loads per lane per tile (K and V)
     static constexpr int NG = D / 16;  // 16-dim output groups
     static constexpr int TILE_U4 = D * 2;
 
-    struct State {
-        u32x4 q[NL];
+    struct Q {
+        u32x4 v[NL];
+    };
+    struct Acc {
         float m, l;
         f32x4 acc[NG];
     };
 
-    static __device__ __forceinline__ void tile(const DecodeArgs& a, State& st, const u32x4* kb,
-                                                const u32x4* vb, int t, int ctx, int lane) {
+    static __device__ __forceinline__ int kv_head(const DecodeArgs&, int row) { return row; }
+
+    static __device__ __forceinline__ void load_q(const DecodeArgs& a, Q& q, int row, int seq,
+                                                  int lane) {
+        const int j = lane >> 4, i = lane & 15;
+        const T* qrow = static_cast<const T*>(a.q) +
+                        (static_cast<size_t>(seq) * a.num_q_heads + row * G + (i % G)) * D;
+#pragma unroll
+        for (int s = 0; s < NL; ++s) q.v[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * j);
+    }
+
+    static __device__ __forceinline__ void reset(Acc& st) {
+        st.m = kNegInf;
+        st.l = 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) st.acc[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+    static __device__ __forceinline__ void tile(const DecodeArgs& a, Acc& st, const Q& q,
+                                                const u32x4* kb, const u32x4* vb, int t, int ctx,
+                                                int lane) {
         const int j = lane >> 4;
         f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NL; ++s)
             S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[s]),
-                                                        __builtin_bit_cast(bf16x8, st.q[s]), S, 0,
+                                                        __builtin_bit_cast(bf16x8, q.v[s]), S, 0,
                                                         0, 0);
         const int tok0 = t * kTile + 4 * j;
         float sc[4];
@@ -339,29 +369,15 @@ struct GroupPath {
         }
     }
 
-    static __device__ void piece(const DecodeArgs& a, int row, int seq, int t0, int t1, bool whole,
-                                 float* rec, int lane) {
-        const int kvh = row;
-        const int G = a.group;
+    static __device__ __forceinline__ void finish(const DecodeArgs& a, Acc& st, int row, int seq,
+                                                  bool whole, float* rec, int lane) {
         const int j = lane >> 4, i = lane & 15;
-        const int ctx = ctx_of(a, seq);
-        State st;
-        const T* qrow = static_cast<const T*>(a.q) +
-                        (static_cast<size_t>(seq) * a.num_q_heads + kvh * G + (i % G)) * D;
-#pragma unroll
-        for (int s = 0; s < NL; ++s) st.q[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * j);
-        st.m = kNegInf;
-        st.l = 0.f;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) st.acc[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        run_tiles(a, st, seq, kvh, t0, t1, ctx, lane);
-        // finish
         float L = st.l;
         L += __shfl_xor(L, 16);
         L += __shfl_xor(L, 32);
         if (i >= G) return;
         if (whole) {
-            T* o = static_cast<T*>(a.out) + (static_cast<size_t>(seq) * a.num_q_heads + kvh * G + i) * D;
+            T* o = static_cast<T*>(a.out) + (static_cast<size_t>(seq) * a.num_q_heads + row * G + i) * D;
             const float inv = 1.f / L;
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
@@ -379,81 +395,207 @@ struct GroupPath {
             }
         }
     }
-
-    static __device__ void run_tiles(const DecodeArgs& a, State& st, int seq, int kvh, int t0,
-                                     int t1, int ctx, int lane);
 };
 
 // ---------------------------------------------------------------------------------
-// The tile loop shared by both paths: gather through the block table with the
-// next tile's loads in flight while the current tile is computed.
-template <class Path, class State>
-__device__ __forceinline__ void tile_loop(const DecodeArgs& a, State& st, int seq, int kvh, int t0,
-                                          int t1, int ctx, int lane) {
-    constexpr int NL = Path::NL;
-    const int tpb = a.tiles_per_block;
-    const int32_t* bt = a.block_tables + static_cast<size_t>(seq) * a.max_blocks;
-    int e_lo = t0 / tpb;
-    const int e_last = (t1 - 1) / tpb;
-    int win = load_window(bt, e_lo, e_last, lane, a.num_blocks);
-    const u32x4* kc = static_cast<const u32x4*>(a.k_cache) + lane;
-    const u32x4* vc = static_cast<const u32x4*>(a.v_cache) + lane;
-    const size_t hkv = static_cast<size_t>(a.num_kv_heads);
-
-    auto tile_off = [&](int t) -> size_t {
-        const int e = t / tpb;
-        if (e - e_lo >= kWave) {
-            e_lo = e;
-            win = load_window(bt, e_lo, e_last, lane, a.num_blocks);
-        }
-        const int blk = __builtin_amdgcn_readlane(win, e - e_lo);
-        return ((static_cast<size_t>(blk) * hkv + kvh) * tpb + (t - e * tpb)) *
-               static_cast<size_t>(Path::TILE_U4);
+// Log-sum-exp merge of the partial records of one split (sequence, row), pieces
+// held by units us .. ue (unit us keeps it in record slot slot_us, the others
+// in slot 0):
+//   M = max_p m_p;  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
+// GH heads share a row.  Pair k = (piece us + k / GH, head k % GH).  First each
+// lane folds its pairs' (m, l) with a running maximum; GH divides the wave width,
+// so lane L only ever sees head L % GH, and an xor reduction over lanes GH apart
+// gives every lane its head's M and sum.  Then each lane owns K = GH * D / 64
+// output elements; the accumulators of up to four pieces are requested at once,
+// and their weights come from the lanes holding the pairs (or from memory when a
+// split has more than 64 pairs).
+template <typename T, int D, int GH>
+__device__ void merge_pieces(const DecodeArgs& a, int row, int seq, int us, int ue, int slot_us,
+                             int lane) {
+    constexpr int K = GH * D / kWave;
+    static_assert(K >= 1 && (GH * D) % kWave == 0 && kWave % GH == 0, "merge shape");
+    constexpr int kMOff = GH * D;  // record: [GH][D] acc, [GH] m, [GH] l
+    constexpr size_t pf = static_cast<size_t>(GH * D + ((2 * GH + 3) & ~3));
+    auto piece = [&](int p) -> const float* {
+        return a.pieces + (static_cast<size_t>(p) * 2 + (p == us ? slot_us : 0)) * pf;
     };
-
-    u32x4 kA[NL], vA[NL], kB[NL], vB[NL];
-    size_t off = tile_off(t0);
-#pragma unroll
-    for (int s = 0; s < NL; ++s) kA[s] = kc[off + s * kWave];
-#pragma unroll
-    for (int s = 0; s < NL; ++s) vA[s] = vc[off + s * kWave];
-    for (int t = t0; t < t1; t += 2) {
-        if (t + 1 < t1) {
-            off = tile_off(t + 1);
-#pragma unroll
-            for (int s = 0; s < NL; ++s) kB[s] = kc[off + s * kWave];
-#pragma unroll
-            for (int s = 0; s < NL; ++s) vB[s] = vc[off + s * kWave];
-        }
-        Path::tile(a, st, kA, vA, t, ctx, lane);
-        if (t + 1 >= t1) break;
-        if (t + 2 < t1) {
-            off = tile_off(t + 2);
-#pragma unroll
-            for (int s = 0; s < NL; ++s) kA[s] = kc[off + s * kWave];
-#pragma unroll
-            for (int s = 0; s < NL; ++s) vA[s] = vc[off + s * kWave];
-        }
-        Path::tile(a, st, kB, vB, t + 1, ctx, lane);
+    const int np = ue - us + 1;
+    const int pairs = np * GH;
+    // (m, l) of this lane's first pair; kept for the weights below
+    float m0 = kNegInf, l0 = 0.f;
+    if (lane < pairs) {
+        const float* r = piece(us + lane / GH);
+        m0 = r[kMOff + lane % GH];
+        l0 = r[kMOff + GH + lane % GH];
     }
-}
-
-template <typename T, int D>
-__device__ void HeadPath<T, D>::run_tiles(const DecodeArgs& a, State& st, int seq, int kvh, int t0,
-                                          int t1, int ctx, int lane) {
-    tile_loop<HeadPath<T, D>, State>(a, st, seq, kvh, t0, t1, ctx, lane);
-}
-
-template <int D>
-__device__ void GroupPath<D>::run_tiles(const DecodeArgs& a, State& st, int seq, int kvh, int t0,
-                                        int t1, int ctx, int lane) {
-    tile_loop<GroupPath<D>, State>(a, st, seq, kvh, t0, t1, ctx, lane);
+    float M = m0, den = l0;
+    for (int k = lane + kWave; k < pairs; k += kWave) {  // splits with more than 64 pairs
+        const float* r = piece(us + k / GH);
+        const float m = r[kMOff + k % GH];
+        const float mn = fmaxf(M, m);
+        den = den * fast_exp2(M - mn) + fast_exp2(m - mn) * r[kMOff + GH + k % GH];
+        M = mn;
+    }
+#pragma unroll
+    for (int o = GH; o < kWave; o <<= 1) {
+        const float Mo = __shfl_xor(M, o), Do = __shfl_xor(den, o);
+        const float mn = fmaxf(M, Mo);
+        // a side with no pairs has M = -inf and den = 0: guard its 2^(-inf - -inf)
+        den = (M == kNegInf ? 0.f : den * fast_exp2(M - mn)) +
+              (Mo == kNegInf ? 0.f : Do * fast_exp2(Mo - mn));
+        M = mn;
+    }
+    // weight of this lane's first pair (pairs < 64: every weight is in some lane)
+    const float w0 = fast_exp2(m0 - M);
+    float Mh[K], acc[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+        Mh[c] = __shfl(M, (kWave * c) / D);  // element c of this lane is lane + 64 c, head 64 c / D
+        acc[c] = 0.f;
+    }
+    int p = us;
+    for (; p + 4 <= ue + 1; p += 4) {
+        float v[4][K];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float* r = piece(p + t);
+#pragma unroll
+            for (int c = 0; c < K; ++c) v[t][c] = r[lane + kWave * c];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int pk = (p + t - us) * GH;
+#pragma unroll
+            for (int c = 0; c < K; ++c) {
+                const int h = (kWave * c) / D;
+                const float w = pairs <= kWave ? __shfl(w0, pk + h)
+                                               : fast_exp2(piece(p + t)[kMOff + h] - Mh[c]);
+                acc[c] = __builtin_fmaf(w, v[t][c], acc[c]);
+            }
+        }
+    }
+    for (; p <= ue; ++p) {
+        const float* r = piece(p);
+        float v[K];
+#pragma unroll
+        for (int c = 0; c < K; ++c) v[c] = r[lane + kWave * c];
+        const int pk = (p - us) * GH;
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            const int h = (kWave * c) / D;
+            const float w = pairs <= kWave ? __shfl(w0, pk + h) : fast_exp2(r[kMOff + h] - Mh[c]);
+            acc[c] = __builtin_fmaf(w, v[c], acc[c]);
+        }
+    }
+    const int qh0 = row * GH;  // group rows hold heads row*G..; per-head rows hold head `row`
+    T* o = static_cast<T*>(a.out) + (static_cast<size_t>(seq) * a.num_q_heads + qh0) * D;
+#pragma unroll
+    for (int c = 0; c < K; ++c) store_out<T>(o + lane + kWave * c, acc[c] / __shfl(den, (kWave * c) / D));
 }
 
 // ---------------------------------------------------------------------------------
-// Pass 1: one wavefront per unit.
+// Walking a unit's tiles.  The line of tiles is addressed by a cursor (row,
+// sequence, tile inside the sequence).  A chunk describes up to 64 consecutive
+// tiles of the walk, one per lane, with everything the loop needs to fetch and
+// fold that tile: its sequence, row, tile index, the sequence's context length
+// and the tile's position in the cache (block-table entry already applied).
+// Building a chunk reads the context lengths of the next 64 sequences and the
+// table entries of its tiles in one parallel round each, so the tile loop
+// itself never waits on a dependent table read, also across sequence ends.
+struct Cursor {
+    int row, seq, t0;
+};
+
+struct Chunk {
+    int n;       // tiles held (uniform)
+    int seq;     // lane k: sequence of tile k
+    int tile;    // lane k: tile index inside its sequence
+    int row;     // lane k: work row
+    int ctx;     // lane k: context length of its sequence
+    int toff;    // lane k: tile index in the cache, (block * Hkv + kv head) * tpb + tile % tpb
+    Cursor next; // where the walk continues after the chunk (uniform)
+};
+
+// Uniform copy of one lane of a chunk.
+struct TileRef {
+    int seq, tile, row, ctx, toff;
+};
+
+__device__ __forceinline__ TileRef tile_ref(const Chunk& c, int k) {
+    TileRef r;
+    r.seq = __builtin_amdgcn_readlane(c.seq, k);
+    r.tile = __builtin_amdgcn_readlane(c.tile, k);
+    r.row = __builtin_amdgcn_readlane(c.row, k);
+    r.ctx = __builtin_amdgcn_readlane(c.ctx, k);
+    r.toff = __builtin_amdgcn_readlane(c.toff, k);
+    return r;
+}
+
+// The chunk of at most min(64, remaining) tiles starting at cursor c.  Rows wrap
+// after sequence S - 1; sequences with no tiles are passed over.  Block IDs
+// outside [0, N) are replaced by 0 so a bad table never addresses outside the pool.
+template <class Path>
+__device__ __forceinline__ Chunk build_chunk(const DecodeArgs& a, Cursor c, int remaining,
+                                             int lane) {
+    const int S = a.num_seqs;
+    // lane k looks at the k-th sequence from the cursor
+    int sk = c.seq + lane;
+    const int rk = c.row + sk / S;
+    sk %= S;
+    const int ctx_k = rk < a.rows ? ctx_of(a, sk) : 0;
+    int n = tiles_of(ctx_k);
+    if (lane == 0) n -= c.t0;
+    const int incl = wave_inclusive_scan(n, lane);
+    const int excl = incl - n;
+    const int avail = __builtin_amdgcn_readlane(incl, kWave - 1);
+    Chunk ch;
+    ch.n = min(min(kWave, remaining), avail);
+    // tile k belongs to the source lane j with excl_j <= k < incl_j
+    int j = 0;
+    for (int src = 0; src < kWave; ++src) {
+        const int lo = __builtin_amdgcn_readlane(excl, src);
+        if (lo >= ch.n) break;
+        if (lane >= lo && lane < __builtin_amdgcn_readlane(incl, src)) j = src;
+    }
+    const int tin = lane - __shfl(excl, j) + (j == 0 ? c.t0 : 0);
+    const int ssk = __shfl(sk, j);
+    const int rr = __shfl(rk, j);
+    ch.seq = ssk;
+    ch.row = rr;
+    ch.tile = tin;
+    ch.ctx = __shfl(ctx_k, j);
+    int toff = 0;
+    if (lane < ch.n) {
+        const int tpb = a.tiles_per_block;
+        const int e = tin / tpb;
+        int blk = a.block_tables[static_cast<size_t>(ssk) * a.max_blocks + e];
+        blk = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
+        toff = (blk * a.num_kv_heads + Path::kv_head(a, rr)) * tpb + (tin - e * tpb);
+    }
+    ch.toff = toff;
+    // the walk after the chunk
+    if (ch.n < avail) {
+        const unsigned long long past = __ballot(incl > ch.n);
+        const int jn = __ffsll(static_cast<long long>(past)) - 1;
+        ch.next.seq = __builtin_amdgcn_readlane(sk, jn);
+        ch.next.row = __builtin_amdgcn_readlane(rk, jn);
+        ch.next.t0 = ch.n - __builtin_amdgcn_readlane(excl, jn) + (jn == 0 ? c.t0 : 0);
+    } else {
+        const int s64 = c.seq + kWave;
+        ch.next.row = c.row + s64 / S;
+        ch.next.seq = s64 % S;
+        ch.next.t0 = 0;
+    }
+    return ch;
+}
+
+// ---------------------------------------------------------------------------------
+// Pass 1: one wavefront per unit.  The loop keeps the next tile's K/V loads
+// (and, when that tile opens a new piece, the new query) in flight while the
+// current tile is folded in.
 template <class Path, typename T, int D>
 __global__ __launch_bounds__(64) void decode_pass1(DecodeArgs a) {
+    constexpr int NL = Path::NL;
     const int lane = threadIdx.x;
     const int u = blockIdx.x;
     const int S = a.num_seqs;
@@ -463,23 +605,21 @@ __global__ __launch_bounds__(64) void decode_pass1(DecodeArgs a) {
     for (int i = u; i < S; i += W)
         if (ctx_of(a, i) == 0) write_zero_seq<T, D>(a, i, lane);
     // Tiles per row.
-    int T_row = 0;
-    for (int base = 0; base < S; base += kWave) {
-        const int i = base + lane;
-        T_row += wave_sum(i < S ? tiles_of(ctx_of(a, i)) : 0);
-    }
-    T_row = uni(T_row);
+    int mine = 0;
+#pragma unroll 4
+    for (int i = lane; i < S; i += kWave) mine += tiles_of(ctx_of(a, i));
+    const int T_row = uni(wave_sum(mine));
     int32_t* rec = a.unit_rec + static_cast<size_t>(u) * kRecInts;
     if (lane == 0) rec[0] = -1;  // overwritten below when the unit holds work
     const int total = a.rows * T_row;
     const int C = (total + W - 1) / W;
     const int start = u * C;
     if (total == 0 || start >= total) return;
-    const int end = min(start + C, total);
-    int row = start / T_row;
-    const int tin = start - row * T_row;
+    const int n_tiles = min(start + C, total) - start;
+    const int row0 = start / T_row;
+    const int tin = start - row0 * T_row;
     // Find the sequence holding tile `tin` of the row.
-    int seq = 0, t0 = 0;
+    int seq0 = 0, t00 = 0;
     {
         int carry = 0;
         for (int base = 0; base < S; base += kWave) {
@@ -489,52 +629,132 @@ __global__ __launch_bounds__(64) void decode_pass1(DecodeArgs a) {
             const unsigned long long hit = __ballot(incl > tin);
             if (hit) {
                 const int f = __ffsll(static_cast<long long>(hit)) - 1;
-                seq = base + f;
-                t0 = tin - __shfl(incl - n, f);
+                seq0 = base + f;
+                t00 = tin - __shfl(incl - n, f);
                 break;
             }
             carry = __shfl(incl, kWave - 1);
         }
     }
-    seq = uni(seq);
-    t0 = uni(t0);
-    int pos = start;
-    bool first = true;
-    while (true) {
-        const int nts = tiles_of(ctx_of(a, seq));
-        const int take = min(nts - t0, end - pos);
-        // Only reachable if context_lens changed under the kernel: stop rather than spin.
-        if (take <= 0) break;
-        const int seq_begin = pos - t0;
-        if (first && lane == 0) {
-            rec[0] = row;
-            rec[1] = seq;
+
+    const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
+    const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
+
+    // ---- fetch side: chunk, next lane of it, tiles issued so far
+    Chunk ch = build_chunk<Path>(a, Cursor{row0, uni(seq0), uni(t00)}, n_tiles, lane);
+    int kf = 0, fetched = 0;
+    int f_seq = -1, f_row = -1;  // piece of the last fetched tile
+    typename Path::Q q, qn;
+
+    struct Buf {
+        u32x4 k[NL], v[NL];
+        TileRef r;
+        bool opens;  // first tile of a piece
+    };
+    Buf A, B;
+
+    auto issue = [&](Buf& b) {
+        // One tile in flight per wave: the previous tile's loads have all returned
+        // before the next tile is requested.  Measured on MI355X, this sustains more
+        // HBM bandwidth than keeping two tiles in flight (the extra requests only
+        // lengthen the memory queues); the unit count then sets the bytes in flight.
+        wait_all_loads();
+        while (kf == ch.n) {  // chunk used up: describe the next tiles (empty chunks only
+                              // arise from runs of sequences with no cached tokens)
+            if (ch.next.row >= a.rows) {
+                // The walk ran past the last row, which only happens if context_lens
+                // changed under the kernel: fold harmless in-pool tiles instead of spinning.
+                ch.n = 1;
+                ch.seq = ch.tile = ch.row = ch.ctx = ch.toff = 0;
+                kf = 0;
+                break;
+            }
+            ch = build_chunk<Path>(a, ch.next, n_tiles - fetched, lane);
+            kf = 0;
+        }
+        b.r = tile_ref(ch, kf);
+        ++kf;
+        ++fetched;
+        // The query of a new piece is requested before the tile, so that waiting
+        // for it never waits for the tile's loads as well.
+        b.opens = (b.r.seq != f_seq) || (b.r.row != f_row);
+        if (b.opens) Path::load_q(a, qn, b.r.row, b.r.seq, lane);
+        f_seq = b.r.seq;
+        f_row = b.r.row;
+        // Uniform tile base (scalar registers) + lane offset: one contiguous KiB per load.
+        const size_t off = static_cast<size_t>(b.r.toff) * Path::TILE_U4;
+        const u32x4* kt = kc + off;
+        const u32x4* vt = vc + off;
+#pragma unroll
+        for (int s = 0; s < NL; ++s) b.k[s] = kt[lane + s * kWave];
+#pragma unroll
+        for (int s = 0; s < NL; ++s) b.v[s] = vt[lane + s * kWave];
+    };
+
+    // ---- compute side: the open piece
+    typename Path::Acc st;
+    int p_seq = -1, p_row = 0, p_t0 = 0, p_last = 0, p_ctx = 0, p_g0 = 0, npieces = 0;
+    auto close_piece = [&]() {
+        const int nts = tiles_of(p_ctx);
+        const bool whole = (p_t0 == 0) && (p_last == nts - 1);
+        float* prec = a.pieces + (static_cast<size_t>(u) * 2 + (npieces == 0 ? 0 : 1)) * pf;
+        if (npieces == 0 && lane == 0) {
+            const int seq_begin = start + p_g0 - p_t0;
+            rec[0] = p_row;
+            rec[1] = p_seq;
             rec[2] = seq_begin;
             rec[3] = seq_begin + nts;
             rec[4] = C;
         }
-        const bool whole = (t0 == 0 && take == nts);
-        float* prec = a.pieces + (static_cast<size_t>(u) * 2 + (first ? 0 : 1)) * pf;
-        Path::piece(a, row, seq, t0, t0 + take, whole, prec, lane);
-        pos += take;
-        first = false;
-        if (pos >= end) break;
-        t0 = 0;
-        do {
-            if (++seq == S) {
-                seq = 0;
-                ++row;
-            }
-        } while (row < a.rows && tiles_of(ctx_of(a, seq)) == 0);
-        if (row >= a.rows) break;
+        Path::finish(a, st, p_row, p_seq, whole, prec, lane);
+        ++npieces;
+    };
+    auto enter = [&](const Buf& b, int g) {
+        if (b.opens) {
+            if (p_seq >= 0) close_piece();
+#pragma unroll
+            for (int s = 0; s < NL; ++s) q.v[s] = qn.v[s];
+            Path::reset(st);
+            p_seq = b.r.seq;
+            p_row = b.r.row;
+            p_t0 = b.r.tile;
+            p_ctx = b.r.ctx;
+            p_g0 = g;
+        }
+        p_last = b.r.tile;
+    };
+
+    // Steady state: every trip folds two tiles and issues the two after them.  The
+    // issues are unconditional inside the loop (the last tiles are peeled off below):
+    // a conditional issue would join paths with different numbers of loads in
+    // flight, and the compiler then waits for all of them before the MFMAs.
+    issue(A);
+    int g = 0;
+    for (; g + 2 < n_tiles; g += 2) {
+        enter(A, g);
+        issue(B);
+        Path::tile(a, st, q, A.k, A.v, A.r.tile, A.r.ctx, lane);
+        enter(B, g + 1);
+        issue(A);
+        Path::tile(a, st, q, B.k, B.v, B.r.tile, B.r.ctx, lane);
     }
+    enter(A, g);
+    if (g + 1 < n_tiles) {
+        issue(B);
+        Path::tile(a, st, q, A.k, A.v, A.r.tile, A.r.ctx, lane);
+        enter(B, g + 1);
+        Path::tile(a, st, q, B.k, B.v, B.r.tile, B.r.ctx, lane);
+    } else {
+        Path::tile(a, st, q, A.k, A.v, A.r.tile, A.r.ctx, lane);
+    }
+    close_piece();
 }
 
 // ---------------------------------------------------------------------------------
-// Pass 2: unit u merges the split sequence whose last piece it holds (its first
-// piece, when that sequence began in an earlier unit and ends inside unit u).
-//   M = max_p m_p;  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
-template <typename T, int D>
+// Pass 2 (separate kernel): unit u merges the split sequence whose last piece it
+// holds (its first piece, when that sequence began in an earlier unit and ends
+// inside unit u).
+template <typename T, int D, int GH>
 __global__ __launch_bounds__(64) void decode_pass2(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int u = blockIdx.x;
@@ -546,27 +766,21 @@ __global__ __launch_bounds__(64) void decode_pass2(DecodeArgs a) {
     const int ustart = u * C;
     if (begin >= ustart || end > ustart + C) return;
     const int us = begin / C;
-    const int slot_us = (begin == us * C) ? 0 : 1;
-    const int GH = a.heads_per_row;
-    const size_t pf = static_cast<size_t>(GH * D + ((2 * GH + 3) & ~3));
-    const int qh0 = row * GH;  // group rows hold heads row*G..; per-head rows hold head `row`
-    T* o = static_cast<T*>(a.out) + (static_cast<size_t>(seq) * a.num_q_heads + qh0) * D;
-    for (int idx = lane; idx < GH * D; idx += kWave) {
-        const int h = idx / D;
-        float M = kNegInf;
-        for (int p = us; p <= u; ++p) {
-            const float* r = a.pieces + (static_cast<size_t>(p) * 2 + (p == us ? slot_us : 0)) * pf;
-            M = fmaxf(M, r[GH * D + h]);
-        }
-        float num = 0.f, den = 0.f;
-        for (int p = us; p <= u; ++p) {
-            const float* r = a.pieces + (static_cast<size_t>(p) * 2 + (p == us ? slot_us : 0)) * pf;
-            const float w = fast_exp2(r[GH * D + h] - M);
-            num = __builtin_fmaf(w, r[idx], num);
-            den = __builtin_fmaf(w, r[GH * D + GH + h], den);
-        }
-        store_out<T>(o + idx, num / den);
+    merge_pieces<T, D, GH>(a, row, seq, us, u, (begin == us * C) ? 0 : 1, lane);
+}
+
+template <typename T, int D>
+hipError_t launch_pass2(const DecodeArgs& a, hipStream_t st) {
+    const dim3 grid(a.num_units), block(kWave);
+    switch (a.heads_per_row) {
+        case 1: hipLaunchKernelGGL((decode_pass2<T, D, 1>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((decode_pass2<T, D, 2>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((decode_pass2<T, D, 4>), grid, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((decode_pass2<T, D, 8>), grid, block, 0, st, a); break;
+        case 16: hipLaunchKernelGGL((decode_pass2<T, D, 16>), grid, block, 0, st, a); break;
+        default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
 }
 
 template <class Path, typename T, int D>
@@ -577,10 +791,21 @@ hipError_t launch_two_pass(const DecodeArgs& a, int passes, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (passes & 2) {
-        hipLaunchKernelGGL((decode_pass2<T, D>), dim3(a.num_units), dim3(kWave), 0, st, a);
+        hipLaunchKernelGGL((decode_pass2<T, D, Path::GH>), dim3(a.num_units), dim3(kWave), 0, st, a);
         return hipGetLastError();
     }
     return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_group(const DecodeArgs& a, int passes, hipStream_t st) {
+    switch (a.group) {
+        case 2: return launch_two_pass<GroupPath<D, 2>, uint16_t, D>(a, passes, st);
+        case 4: return launch_two_pass<GroupPath<D, 4>, uint16_t, D>(a, passes, st);
+        case 8: return launch_two_pass<GroupPath<D, 8>, uint16_t, D>(a, passes, st);
+        case 16: return launch_two_pass<GroupPath<D, 16>, uint16_t, D>(a, passes, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -589,8 +814,8 @@ hipError_t launch_decode(int dtype, int head_dim, bool use_group_kernel, const D
                          int passes, hipStream_t stream) {
     if (dtype == 1) {  // bf16
         if (use_group_kernel) {
-            if (head_dim == 128) return launch_two_pass<GroupPath<128>, uint16_t, 128>(a, passes, stream);
-            if (head_dim == 64) return launch_two_pass<GroupPath<64>, uint16_t, 64>(a, passes, stream);
+            if (head_dim == 128) return launch_group<128>(a, passes, stream);
+            if (head_dim == 64) return launch_group<64>(a, passes, stream);
         } else {
             if (head_dim == 128) return launch_two_pass<HeadPath<uint16_t, 128>, uint16_t, 128>(a, passes, stream);
             if (head_dim == 64) return launch_two_pass<HeadPath<uint16_t, 64>, uint16_t, 64>(a, passes, stream);

@@ -189,3 +189,46 @@ def test_full_size_config_sampled(name):
     ref = b.expected(pick)
     assert_close(to_float64(out[pick], spec.dtype), ref, spec.dtype, f"{name} sampled {pick}")
     assert np.isfinite(to_float64(out, spec.dtype)).all()
+
+
+# ----------------------------------------------------------------------------- two calls vs one
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,units", [("bf16", 32, 8, 128, 37), ("bf16", 16, 16, 128, 64),
+                                                 ("bf16", 16, 8, 64, 19), ("f32", 4, 2, 128, 11)])
+def test_partial_then_merge_equals_single_call_bitwise(dtype, Hq, Hkv, D, units):
+    """_partial then _merge on one stream is the single call, bit for bit."""
+    rng = gen.stream(51, 1)
+    ctx = rng.integers(1, 900, 10)
+    ctx[3] = 0
+    spec = ops.CacheSpec(num_blocks=1024, block_size=16, num_kv_heads=Hkv, head_dim=D, dtype=dtype)
+    b = Batch(spec, ctx, Hq, seed=51, free_order=gen.pool_permutation(5, 1024))
+    single = b.run(num_units=units)
+    ws = ops.decode_workspace(spec, Hq, units)
+    out = torch.full((b.S, Hq, D), float("nan"), dtype=spec.torch_dtype, device="cuda")
+    args = (spec, out, b.q, b.cache.k, b.cache.v, b.tables, b.ctx_dev, 1 / math.sqrt(D), units, ws)
+    ops.paged_attn_decode_partial(*args)
+    ops.paged_attn_decode_merge(*args)
+    torch.cuda.synchronize()
+    two = to_storage(out)
+    assert np.array_equal(single.view(np.uint8), two.view(np.uint8))
+    assert_close(to_float64(single, dtype), b.expected(), dtype, "single call")
+
+
+def test_reused_workspace_across_calls():
+    """One workspace serves many calls with different lengths and unit counts, and
+    every output of every call is written (outputs start as NaN)."""
+    spec = ops.CacheSpec(num_blocks=2048, block_size=16, num_kv_heads=8, head_dim=128, dtype="bf16")
+    ws = ops.decode_workspace(spec, 32, 300)
+    rng = gen.stream(52, 1)
+    for trial in range(4):
+        ctx = rng.integers(1, 1500, 9)
+        b = Batch(spec, ctx, 32, seed=60 + trial, free_order=gen.pool_permutation(6, 2048))
+        for units in (300, 41, 300, 7, 41, 299):
+            out = torch.full((b.S, 32, 128), float("nan"), dtype=spec.torch_dtype, device="cuda")
+            ops.paged_attn_decode(spec, out, b.q, b.cache.k, b.cache.v, b.tables, b.ctx_dev,
+                                  1 / math.sqrt(128), units, ws)
+            torch.cuda.synchronize()
+            fresh = b.run(num_units=units)
+            assert np.array_equal(to_storage(out).view(np.uint8), fresh.view(np.uint8)), (trial, units)
+        assert_close(to_float64(fresh, "bf16"), b.expected(), "bf16", f"trial {trial}")
