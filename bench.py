@@ -166,7 +166,8 @@ def main():
     spec = ops.CacheSpec(cfg.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_dim, cfg.dtype)
     S, Hq, Hkv, D, B = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     steps, warm = args.steps, args.warmup
-    total_steps = steps + warm
+    prof_steps = 10  # untimed steps for the per-launch breakdown, after the timed region
+    total_steps = steps + warm + prof_steps
 
     # ---------------------------------------------------------------- resident inputs
     t0 = time.time()
@@ -222,11 +223,14 @@ def main():
         f"{units} units")
 
     # ---------------------------------------------------------------- per-step staging
-    R = 4  # ring of pinned metadata buffers
+    # A ring of pinned host buffers holds each step's metadata; the cache-write
+    # kernel reads it in place (no separate host-to-device copy) and forwards the
+    # context lengths to the device array the decode kernels read.
+    R = 4
     words = S * 2 + S + 3 * S + 2 * S  # int32 words: slots (int64), ctx, updates, cow pairs
     pin = [torch.empty(words, dtype=torch.int32, pin_memory=True) for _ in range(R)]
-    dev = [torch.empty(words, dtype=torch.int32, device="cuda") for _ in range(R)]
     ring_ev = [None] * R
+    ctx_dev = torch.from_numpy(ctx0.astype(np.int32)).cuda()
 
     def views(buf):
         return (buf[:2 * S].view(torch.int64), buf[2 * S:3 * S], buf[3 * S:6 * S].view(S, 3),
@@ -236,71 +240,96 @@ def main():
     stream = torch.cuda.current_stream()
     kv_per_tok = cfg.kv_bytes_per_token()
     ev = []
+    host = []  # per timed step: (host bookkeeping + staging, whole host side) seconds
 
-    def step(n, timed):
+    # Every launch of every step is bound once (arguments converted up front); the
+    # per-step metadata has a fixed shape (a copy-on-write row and a table-update row
+    # per sequence, -1 when there is none), so a step's launches never change form.
+    calls = []
+    for n in range(total_steps):
+        hs, hc, hu, hp = views(pin[n % R])
+        calls.append((
+            ops.bind_append_tokens(spec, ks[n], vs[n], hs, cache.k, cache.v, cow_pairs=hp,
+                                   block_tables=tables, table_updates=hu, lens_in=hc,
+                                   lens_out=ctx_dev),
+            ops.bind_decode(spec, out, qs[n], cache.k, cache.v, tables, ctx_dev, cfg.scale, units,
+                            ws, stage="partial"),
+            ops.bind_decode(spec, out, qs[n], cache.k, cache.v, tables, ctx_dev, cfg.scale, units,
+                            ws, stage="merge")))
+
+    def step(n, mode):
+        """mode "warm": no timing events; "timed": events around pass 1 only (the
+        kernel the roofline is taken on); "profile": events around every launch."""
+        h0 = time.perf_counter()
         # a1: host bookkeeping in the library allocator
         st, done, slots, cows, nb, nc = cache.alloc.append_batch(seq_ids)
         if st != 0 or done != S:
             raise RuntimeError(f"append_batch failed at step {n}: status {st}")
         ctx_now[:] += 1
-        upd_rows = np.nonzero(nb >= 0)[0]
-        cow_rows = np.nonzero(cows[:, 0] >= 0)[0]
-        # a2: one host-to-device copy of the step's metadata
+        # a2: the step's metadata into a pinned ring slot the write kernel reads in place
         r = n % R
         if ring_ev[r] is not None:
             ring_ev[r].synchronize()
-        ps, pc, pu, pp = views(pin[r])
-        ps.numpy()[:] = slots
-        pc.numpy()[:] = ctx_now
-        if len(upd_rows):
-            pu.numpy()[:len(upd_rows)] = np.stack([upd_rows, nc[upd_rows], nb[upd_rows]], 1)
-        if len(cow_rows):
-            pp.numpy()[:len(cow_rows)] = cows[cow_rows]
-        dev[r].copy_(pin[r], non_blocking=True)
-        e = torch.cuda.Event()
-        e.record(stream)
-        ring_ev[r] = e
-        ds, dc, du, dp = views(dev[r])
-        if timed:
-            e_start = torch.cuda.Event(enable_timing=True)
-            e_start.record(stream)
-        # a3: copy-on-write block copies, then the changed table entries
-        if len(cow_rows):
-            ops.copy_blocks(spec, cache.k, cache.v, dp[:len(cow_rows)])
-        if len(upd_rows):
-            ops.update_block_tables(tables, du[:len(upd_rows)])
-        # a4: cache write of the step's new tokens
-        ops.reshape_and_cache(spec, ks[n], vs[n], ds, cache.k, cache.v)
-        # a5-a11: decode attention, pass 1 (gather + attention) then pass 2 (merge)
-        if timed:
-            e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        ps, pc, pu, pp = (x.numpy() for x in views(pin[r]))
+        ps[:] = slots
+        pc[:] = ctx_now
+        pu[:, 0] = np.where(nb >= 0, seq_ids, -1)  # (row, column, block); row -1 = no update
+        pu[:, 1] = nc
+        pu[:, 2] = nb
+        pp[:] = cows  # one (src, dst) row per token, (-1, -1) = no copy
+        h1 = time.perf_counter()
+        append, partial, merge = calls[n]
+        timing = mode != "warm"
+        if timing:
+            e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+        if mode == "profile":
+            e0.record(stream)
+        # a3 + a4: copy-on-write block copies, the changed table entries, the cache
+        # write of the step's new tokens and the context lengths, in one launch
+        append()
+        if timing:
             e1.record(stream)
-        ops.paged_attn_decode_partial(spec, out, qs[n], cache.k, cache.v, tables, dc, cfg.scale,
-                                      units, ws)
-        if timed:
+        else:
+            e1 = torch.cuda.Event()
+            e1.record(stream)
+        ring_ev[r] = e1  # the ring slot is free again once the write launch has read it
+        # a5-a11: decode attention, pass 1 (gather + attention) then pass 2 (merge)
+        partial()
+        if timing:
             e2.record(stream)
-        ops.paged_attn_decode_merge(spec, out, qs[n], cache.k, cache.v, tables, dc, cfg.scale,
-                                    units, ws)
-        if timed:
+        merge()
+        if mode == "profile":
             e3.record(stream)
-            ev.append((e_start, e1, e2, e3, int(ctx_now.sum())))
+        if timing:
+            ev[mode].append((e0, e1, e2, e3, int(ctx_now.sum())))
+        if mode == "timed":
+            host.append((h1 - h0, time.perf_counter() - h0))
 
+    ev = {"timed": [], "profile": []}
     for n in range(warm):
-        step(n, False)
+        step(n, "warm")
     torch.cuda.synchronize()
     log(f"warmup done ({warm} steps)")
     t0 = time.perf_counter()
-    for n in range(warm, total_steps):
-        step(n, True)
+    for n in range(warm, warm + steps):
+        step(n, "timed")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {steps} steps in {wall * 1e3:.2f} ms")
+    # untimed per-launch breakdown: events around every launch perturb the stream,
+    # so they stay out of the timed region
+    for n in range(warm + steps, total_steps):
+        step(n, "profile")
+    torch.cuda.synchronize()
 
-    tok = np.array([e[4] for e in ev], dtype=np.float64)
+    tok = np.array([e[4] for e in ev["timed"]], dtype=np.float64)
     kv_bytes = tok * kv_per_tok
-    t_write = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    t_p1 = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-    t_attn = np.array([e[1].elapsed_time(e[3]) for e in ev]) * 1e-3
+    t_p1 = np.array([e[1].elapsed_time(e[2]) for e in ev["timed"]]) * 1e-3
+    pe = ev["profile"]
+    pbytes = np.array([e[4] for e in pe], dtype=np.float64) * kv_per_tok
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in pe]) * 1e-3
+    t_pp1 = np.array([e[1].elapsed_time(e[2]) for e in pe]) * 1e-3
+    t_attn = np.array([e[1].elapsed_time(e[3]) for e in pe]) * 1e-3
     value = float(kv_bytes.sum() / wall / 1e9)
     p1_gbps = float(np.median(kv_bytes / t_p1) / 1e9)
     result = {
@@ -321,10 +350,17 @@ def main():
                    "sum_ctx_first_step": int(tok[0]), "units": units, "seed": cfg.seed},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "us_per_step": round(wall / steps * 1e6, 2),
-        "device_us_per_step_median": round(float(np.median(t_write + t_attn)) * 1e6, 2),
-        "write_us_median": round(float(np.median(t_write)) * 1e6, 2),
-        "attn_us_median": round(float(np.median(t_attn)) * 1e6, 2),
-        "attn_gbps_median": round(float(np.median(kv_bytes / t_attn) / 1e9), 2),
+        "breakdown": {
+            "note": f"{len(pe)} untimed steps after the timed region, events around every launch",
+            "device_us_per_step_median": round(float(np.median(t_write + t_attn)) * 1e6, 2),
+            "write_us_median": round(float(np.median(t_write)) * 1e6, 2),
+            "pass1_us_median": round(float(np.median(t_pp1)) * 1e6, 2),
+            "attn_us_median": round(float(np.median(t_attn)) * 1e6, 2),
+            "pass2_us_median": round(float(np.median(t_attn - t_pp1)) * 1e6, 2),
+            "attn_gbps_median": round(float(np.median(pbytes / t_attn) / 1e9), 2),
+        },
+        "host_bookkeeping_us_median": round(float(np.median([h[0] for h in host])) * 1e6, 2),
+        "host_step_us_median": round(float(np.median([h[1] for h in host])) * 1e6, 2),
         "roofline": {
             "kernel": "decode_pass1",
             "bound": "hbm",

@@ -128,6 +128,36 @@ pa_status pa_update_block_tables(int32_t* block_tables, int32_t num_rows,
                                  int32_t num_updates, void* stream);
 
 /*
+ * pa_append_tokens - every write of one decode step in a single launch: the
+ * copy-on-write block copies, the block-table updates, the new tokens' scatter
+ * (the writes that follow each forward step, [P2] 调度流程 step 4; the sharing
+ * that copy-on-write preserves, [P2] 优势 > 3. 支持共享) and the upload of the
+ * context lengths the next decode call reads.
+ *   k, v, slot_mapping, num_tokens   as for pa_reshape_and_cache
+ *   cow_pairs      [num_tokens][2] int32 (src, dst) or NULL: before token t is
+ *                  written, block src is copied onto block dst (whole block, K and
+ *                  V); (-1, -1) or an ID outside [0, N) = no copy
+ *   block_tables   device, [num_rows][max_blocks_per_seq] int32, updated in place
+ *   table_updates  [num_updates][3] int32 (row, column, block) or NULL; entries
+ *                  outside the table are skipped; no two may name one entry
+ *   lens_in, lens_out, num_lens   lens_out[i] = lens_in[i] for i < num_lens
+ *                  (lens_out device; NULL/0 = nothing)
+ * slot_mapping, cow_pairs, table_updates and lens_in may be device memory or
+ * pinned host memory (each element is read once), so a step's host-built
+ * metadata needs no separate copy.  The result equals pa_copy_blocks (all pairs),
+ * pa_update_block_tables, then pa_reshape_and_cache, provided that sequences
+ * which share a block hold the same number of tokens in it (always the case for
+ * blocks shared through the allocator's fork).
+ */
+pa_status pa_append_tokens(const pa_cache_desc* desc, const void* k, const void* v,
+                           const int64_t* slot_mapping, const int32_t* cow_pairs,
+                           int32_t num_tokens, void* k_cache, void* v_cache,
+                           int32_t* block_tables, int32_t num_rows, int32_t max_blocks_per_seq,
+                           const int32_t* table_updates, int32_t num_updates,
+                           const int32_t* lens_in, int32_t* lens_out, int32_t num_lens,
+                           void* stream);
+
+/*
  * Decode attention.
  *
  * For each sequence i and query head j, with L = context_lens[i],

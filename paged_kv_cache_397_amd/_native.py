@@ -43,6 +43,8 @@ SIGNATURES = {
     "pa_reshape_and_cache": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "pa_copy_blocks": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp]),
     "pa_update_block_tables": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_i32, c_vp]),
+    "pa_append_tokens": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i32,
+                                 c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp]),
     "pa_decode_workspace_bytes": (c_sz, [P_desc, c_i32, c_i32]),
     "pa_decode_default_units": (c_i32, []),
     "pa_paged_attn_decode": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,

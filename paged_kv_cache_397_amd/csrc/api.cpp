@@ -119,6 +119,38 @@ pa_status pa_copy_blocks(const pa_cache_desc* d, void* k_cache, void* v_cache,
                                             static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_append_tokens(const pa_cache_desc* d, const void* k, const void* v,
+                           const int64_t* slot_mapping, const int32_t* cow_pairs,
+                           int32_t num_tokens, void* k_cache, void* v_cache,
+                           int32_t* block_tables, int32_t num_rows, int32_t max_blocks_per_seq,
+                           const int32_t* table_updates, int32_t num_updates,
+                           const int32_t* lens_in, int32_t* lens_out, int32_t num_lens,
+                           void* stream) {
+    pa_status st = check_desc(d);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0 || num_updates < 0 || num_rows < 0 || max_blocks_per_seq < 0 ||
+        num_lens < 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_tokens == 0 && num_updates == 0 && num_lens == 0) return PA_OK;
+    if (num_tokens > 0) {
+        if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+        if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+            !aligned(slot_mapping, 8) || (cow_pairs && !aligned(cow_pairs, 4)))
+            return PA_ERR_INVALID_ARG;
+        if (num_tokens > 2147483647 / 4 || d->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+    }
+    if (num_updates > 0 && (!block_tables || !table_updates || !aligned(block_tables, 4) ||
+                            !aligned(table_updates, 4)))
+        return PA_ERR_INVALID_ARG;
+    if (num_lens > 0 && (!lens_in || !lens_out || !aligned(lens_in, 4) || !aligned(lens_out, 4)))
+        return PA_ERR_INVALID_ARG;
+    return from_hip(pkv::launch_append_tokens(
+        d->dtype, d->head_dim, d->block_size, d->num_kv_heads, d->num_blocks, k, v, slot_mapping,
+        num_tokens > 0 ? cow_pairs : nullptr, num_tokens, k_cache, v_cache, block_tables, num_rows,
+        max_blocks_per_seq, table_updates, num_updates, lens_in, lens_out, num_lens,
+        static_cast<hipStream_t>(stream)));
+}
+
 pa_status pa_update_block_tables(int32_t* block_tables, int32_t num_rows,
                                  int32_t max_blocks_per_seq, const int32_t* updates,
                                  int32_t num_updates, void* stream) {

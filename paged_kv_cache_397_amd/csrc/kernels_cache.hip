@@ -79,6 +79,89 @@ __global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict_
     tables[static_cast<int64_t>(r) * cols + c] = upd[3 * k + 2];
 }
 
+// One decode step's writes in one launch.  Workgroup (t, h) first copies KV head
+// h's part of the block that token t's copy-on-write pair names (if any), then
+// scatters token t's K and V for head h; every workgroup applies its share of the
+// block-table updates and of the context-length copy.  A head's part of a block is
+// one contiguous region of each cache array (tiles are ordered block -> head ->
+// tile), so the copy and the token's write for that head never leave the workgroup.
+// Another token's in-place write into the copy source can land before the copy
+// reads it; it is then carried into the copy at the offset the copying token itself
+// writes next (sequences that share a block hold the same number of tokens in it),
+// so the final bytes equal copy-all, then write-all.  The metadata arrays may live
+// in pinned host memory: each element is read once.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void append_tokens_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const int64_t* __restrict__ slots,
+    const int32_t* __restrict__ cow, int num_tokens, T* __restrict__ k_cache,
+    T* __restrict__ v_cache, int num_kv_heads, int block_size, int num_blocks,
+    int32_t* __restrict__ tables, int rows, int cols, const int32_t* __restrict__ upd,
+    int num_updates, const int32_t* __restrict__ lens_in, int32_t* __restrict__ lens_out,
+    int num_lens) {
+    constexpr int X = 16 / sizeof(T);
+    constexpr int E = X / 4;
+    const int t = blockIdx.x, h = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int wg = blockIdx.y * gridDim.x + blockIdx.x;
+    const int nwg = gridDim.x * gridDim.y;
+    for (int n = wg * D + tid; n < num_updates; n += nwg * D) {
+        const int r = upd[3 * n], c = upd[3 * n + 1];
+        if (r >= 0 && r < rows && c >= 0 && c < cols) tables[static_cast<int64_t>(r) * cols + c] = upd[3 * n + 2];
+    }
+    for (int n = wg * D + tid; n < num_lens; n += nwg * D) lens_out[n] = lens_in[n];
+    if (t >= num_tokens) return;
+    const int tpb = block_size / kTile;
+    const int64_t head_u4 = static_cast<int64_t>(tpb) * kTile * D * sizeof(T) / 16;  // one head of one block
+    if (cow) {
+        const int src = cow[2 * t], dst = cow[2 * t + 1];
+        if (src >= 0 && src < num_blocks && dst >= 0 && dst < num_blocks && src != dst) {
+            const int64_t so = (static_cast<int64_t>(src) * num_kv_heads + h) * head_u4;
+            const int64_t dof = (static_cast<int64_t>(dst) * num_kv_heads + h) * head_u4;
+            const u32x4* ks = reinterpret_cast<const u32x4*>(k_cache) + so;
+            const u32x4* vs = reinterpret_cast<const u32x4*>(v_cache) + so;
+            u32x4* kd = reinterpret_cast<u32x4*>(k_cache) + dof;
+            u32x4* vd = reinterpret_cast<u32x4*>(v_cache) + dof;
+            for (int64_t i = tid; i < head_u4; i += D) {
+                kd[i] = ks[i];
+                vd[i] = vs[i];
+            }
+            // the copy's stores complete before any thread writes the token over them
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
+        __syncthreads();
+    }
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= static_cast<int64_t>(num_blocks) * block_size) return;
+    const int64_t b = slot / block_size;
+    const int o = static_cast<int>(slot - b * block_size);
+    const int ti = o & 15;
+    const int j = ti >> 2, r = ti & 3;
+    const int d = tid;
+    const size_t tile_base =
+        ((static_cast<size_t>(b) * num_kv_heads + h) * tpb + (o >> 4)) * (kTile * D);
+    const size_t src = (static_cast<size_t>(t) * num_kv_heads + h) * D;
+    const int m = d / (16 * E), ee = (d >> 4) % E, i = d & 15;
+    v_cache[tile_base + ((((m * 4 + j) * 16 + i) * E + ee) * 4 + r)] = v[src + d];
+    if (d % X == 0)
+        *reinterpret_cast<u32x4*>(k_cache + tile_base + ((d / X) * 16 + ti) * X) =
+            *reinterpret_cast<const u32x4*>(k + src + d);
+}
+
+template <typename T, int D>
+hipError_t launch_append(const void* k, const void* v, const int64_t* slots, const int32_t* cow,
+                         int num_tokens, void* kc, void* vc, int hkv, int bs, int nb,
+                         int32_t* tables, int rows, int cols, const int32_t* upd, int n_upd,
+                         const int32_t* lens_in, int32_t* lens_out, int n_lens, hipStream_t st) {
+    const int extra = (n_upd > n_lens ? n_upd : n_lens);
+    const dim3 grid = num_tokens > 0 ? dim3(num_tokens, hkv) : dim3((extra + D - 1) / D, 1);
+    if (grid.x == 0) return hipSuccess;
+    hipLaunchKernelGGL((append_tokens_kernel<T, D>), grid, dim3(D), 0, st,
+                       static_cast<const T*>(k), static_cast<const T*>(v), slots, cow, num_tokens,
+                       static_cast<T*>(kc), static_cast<T*>(vc), hkv, bs, nb, tables, rows, cols,
+                       upd, n_upd, lens_in, lens_out, n_lens);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_rc(const void* k, const void* v, const int64_t* slots, int num_tokens,
                      void* kc, void* vc, int hkv, int bs, int nb, hipStream_t st) {
@@ -107,6 +190,23 @@ hipError_t launch_reshape_and_cache(int dtype, int head_dim, int block_size, int
                                               num_kv_heads, block_size, num_blocks, stream)
                    : launch_rc<uint16_t, 128>(k, v, slots, num_tokens, k_cache, v_cache,
                                               num_kv_heads, block_size, num_blocks, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_append_tokens(int dtype, int head_dim, int block_size, int num_kv_heads,
+                                int num_blocks, const void* k, const void* v,
+                                const int64_t* slots, const int32_t* cow, int num_tokens,
+                                void* k_cache, void* v_cache, int32_t* tables, int rows, int cols,
+                                const int32_t* upd, int num_updates, const int32_t* lens_in,
+                                int32_t* lens_out, int num_lens, hipStream_t stream) {
+    const bool f32 = dtype == 0;
+#define PKV_APPEND(T, D)                                                                      \
+    launch_append<T, D>(k, v, slots, cow, num_tokens, k_cache, v_cache, num_kv_heads,       \
+                        block_size, num_blocks, tables, rows, cols, upd, num_updates,        \
+                        lens_in, lens_out, num_lens, stream)
+    if (head_dim == 64) return f32 ? PKV_APPEND(uint32_t, 64) : PKV_APPEND(uint16_t, 64);
+    if (head_dim == 128) return f32 ? PKV_APPEND(uint32_t, 128) : PKV_APPEND(uint16_t, 128);
+#undef PKV_APPEND
     return hipErrorInvalidValue;
 }
 

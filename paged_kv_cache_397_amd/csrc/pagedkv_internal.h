@@ -44,6 +44,12 @@ hipError_t launch_reshape_and_cache(int dtype, int head_dim, int block_size, int
                                     int num_blocks, const void* k, const void* v,
                                     const int64_t* slots, int num_tokens, void* k_cache,
                                     void* v_cache, hipStream_t stream);
+hipError_t launch_append_tokens(int dtype, int head_dim, int block_size, int num_kv_heads,
+                                int num_blocks, const void* k, const void* v,
+                                const int64_t* slots, const int32_t* cow, int num_tokens,
+                                void* k_cache, void* v_cache, int32_t* tables, int rows, int cols,
+                                const int32_t* upd, int num_updates, const int32_t* lens_in,
+                                int32_t* lens_out, int num_lens, hipStream_t stream);
 hipError_t launch_copy_blocks(int dtype, int head_dim, int block_size, int num_kv_heads,
                               int num_blocks, void* k_cache, void* v_cache, const int32_t* pairs,
                               int num_pairs, hipStream_t stream);

@@ -55,6 +55,19 @@ def _dev(t: torch.Tensor, name: str, dtype=None):
     return t.data_ptr()
 
 
+def _acc(t: torch.Tensor, name: str, dtype=None):
+    """Device pointer of a tensor the GPU may read: a GPU tensor or pinned host memory."""
+    if t.is_cuda:
+        return _dev(t, name, dtype)
+    if not t.is_pinned():
+        raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
 def cache_bytes(spec: CacheSpec) -> int:
     return int(N.lib().pa_cache_bytes(ctypes.byref(spec.desc())))
 
@@ -87,6 +100,43 @@ def copy_blocks(spec: CacheSpec, k_cache, v_cache, pairs, stream=None):
         _dev(v_cache, "v_cache", spec.torch_dtype), _dev(pairs, "pairs", torch.int32), n,
         _stream(stream))
     N.check(st, "pa_copy_blocks")
+
+
+def _append_args(spec, k, v, slot_mapping, k_cache, v_cache, cow_pairs, block_tables,
+                 table_updates, lens_in, lens_out, stream):
+    T = slot_mapping.numel()
+    if tuple(k.shape) != (T, spec.num_kv_heads, spec.head_dim) or k.shape != v.shape:
+        raise ValueError("k and v must be [T, Hkv, D]")
+    if cow_pairs is not None and cow_pairs.numel() != 2 * T:
+        raise ValueError("cow_pairs must be [T, 2]")
+    n_upd = 0 if table_updates is None else table_updates.numel() // 3
+    rows, cols = (0, 0) if block_tables is None else tuple(block_tables.shape)
+    n_lens = 0 if lens_in is None else lens_in.numel()
+    if n_lens and (lens_out is None or lens_out.numel() < n_lens):
+        raise ValueError("lens_out must hold lens_in")
+    return (ctypes.byref(spec.desc()), _dev(k, "k", spec.torch_dtype),
+            _dev(v, "v", spec.torch_dtype), _acc(slot_mapping, "slot_mapping", torch.int64),
+            None if cow_pairs is None else _acc(cow_pairs, "cow_pairs", torch.int32), T,
+            _dev(k_cache, "k_cache", spec.torch_dtype), _dev(v_cache, "v_cache", spec.torch_dtype),
+            None if block_tables is None else _dev(block_tables, "block_tables", torch.int32),
+            rows, cols,
+            None if n_upd == 0 else _acc(table_updates, "table_updates", torch.int32), n_upd,
+            None if n_lens == 0 else _acc(lens_in, "lens_in", torch.int32),
+            None if n_lens == 0 else _dev(lens_out, "lens_out", torch.int32), n_lens,
+            _stream(stream))
+
+
+def append_tokens(spec: CacheSpec, k, v, slot_mapping, k_cache, v_cache, cow_pairs=None,
+                  block_tables=None, table_updates=None, lens_in=None, lens_out=None,
+                  stream=None):
+    """One launch for a decode step's writes: copy-on-write copies (cow_pairs [T, 2],
+    row t for token t, -1 = none), table updates ([n, 3] rows (row, column, block)),
+    the scatter of k[t], v[t] ([T, Hkv, D]) into slot_mapping[t], and lens_out[:] =
+    lens_in.  slot_mapping, cow_pairs, table_updates and lens_in may be pinned host
+    tensors."""
+    args = _append_args(spec, k, v, slot_mapping, k_cache, v_cache, cow_pairs, block_tables,
+                        table_updates, lens_in, lens_out, stream)
+    N.check(N.lib().pa_append_tokens(*args), "pa_append_tokens")
 
 
 def update_block_tables(block_tables, updates, stream=None):
@@ -164,3 +214,55 @@ def paged_attn_decode_merge(spec: CacheSpec, out, q, k_cache, v_cache, block_tab
         raise ValueError("the partial/merge split needs an explicit shared workspace")
     return _decode("pa_paged_attn_decode_merge", spec, out, q, k_cache, v_cache, block_tables,
                    context_lens, scale, num_units, workspace, stream)
+
+
+class BoundCall:
+    """A library call with every argument converted once, for tight serving loops:
+    calling it costs one foreign-function call and a status check.  The buffers it
+    names must outlive it; the stream is captured at bind time."""
+
+    __slots__ = ("_fn", "_args", "_name", "_keep")
+
+    def __init__(self, name: str, args, keep=None):
+        self._name = name
+        self._fn = getattr(N.lib(), name)
+        self._args = tuple(args)
+        self._keep = keep  # objects the converted arguments point into (the descriptor)
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            N.check(st, self._name)
+
+
+def bind_append_tokens(spec: CacheSpec, k, v, slot_mapping, k_cache, v_cache, cow_pairs=None,
+                       block_tables=None, table_updates=None, lens_in=None, lens_out=None,
+                       stream=None) -> BoundCall:
+    """append_tokens with its arguments fixed (same meaning as append_tokens)."""
+    args = _append_args(spec, k, v, slot_mapping, k_cache, v_cache, cow_pairs, block_tables,
+                        table_updates, lens_in, lens_out, stream)
+    return BoundCall("pa_append_tokens", args, keep=args[0])
+
+
+def bind_decode(spec: CacheSpec, out, q, k_cache, v_cache, block_tables, context_lens,
+                scale: float | None, num_units: int, workspace, stage: str = "both",
+                stream=None) -> BoundCall:
+    """paged_attn_decode (stage "both"), or its first ("partial") or second ("merge")
+    kernel, with its arguments fixed."""
+    fn = {"both": "pa_paged_attn_decode", "partial": "pa_paged_attn_decode_partial",
+          "merge": "pa_paged_attn_decode_merge"}[stage]
+    S, Hq, D = q.shape
+    if D != spec.head_dim or tuple(out.shape) != (S, Hq, D):
+        raise ValueError("q and out must be [S, Hq, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [S, maxB] and context_lens [S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    desc = spec.desc()
+    return BoundCall(fn, (
+        ctypes.byref(desc), _dev(out, "out", spec.torch_dtype), _dev(q, "q", spec.torch_dtype),
+        _dev(k_cache, "k_cache", spec.torch_dtype), _dev(v_cache, "v_cache", spec.torch_dtype),
+        _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, block_tables.shape[1],
+        ctypes.c_float(scale), int(num_units), _dev(workspace, "workspace"), workspace.numel(),
+        _stream(stream)), keep=desc)
