@@ -1,0 +1,141 @@
+"""Oracle model of the continuous-batching loop over a serving trace (test
+infrastructure).
+
+What the pages fix:
+
+* Iteration-level scheduling: every step first removes the requests that have
+  finished and gives their pages back, then admits waiting requests while free
+  pages remain, then runs one forward step for every running request and
+  appends each one's new token (hihuo.com "vLLM 原理：PagedAttention 和
+  Continuous Batching", vLLM 的调度 > 调度流程; ksqn.cn "大模型推理性能优化：
+  PagedAttention与Continuous Batching原理与实践", section 2.3).
+* When memory runs short a low-priority request is suspended, its pages are
+  released for the others, and it resumes later by recomputing its cache
+  (hihuo.com page, Preemption（抢占）, recompute mode).
+
+Readings where the pages are silent (the library's scheduler takes the same):
+
+* Arrivals join the tail of the waiting queue; admission is first come, first
+  served, and stops at the first request whose prompt does not fit in the free
+  blocks (head-of-line blocking).  The pseudo-code pops from a Python list; it
+  is read as FCFS because the allocation sample on the same pages is FIFO.
+* Admission allocates blocks for the whole prompt at once; the prompt is then
+  written in chunks of at most `chunk` tokens, one chunk per request per step,
+  in admission order.  Prefill attention itself is not modelled.
+* A request decodes from the step after its prompt is fully written; each
+  decode step appends one token (its slot reserved by the allocator, with a
+  new block when the token crosses a block boundary) and attends over every
+  cached token, the new one included.  It finishes when it has produced its
+  output length, and is released at the start of the next step.
+* Decode appends run in admission order.  When an append finds no free block,
+  the running request admitted last (the lowest first-come priority, possibly
+  the requester itself) is preempted: its blocks are released, and it goes back
+  to the head of the waiting queue with its prompt extended by the tokens it
+  has generated so far (recompute).  The append is then retried.
+
+Pins: a hand-worked trace on a four-block pool (tests/test_scheduler.py) that
+exercises admission, chunking, release, head-of-line blocking, and preemption
+of another request and of the requester itself; conservation of blocks after
+every step; the library scheduler equals this model step by step.
+"""
+
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass, field
+
+from .allocator_model import AllocatorModel, OutOfBlocks
+
+
+@dataclass
+class Request:
+    rid: int
+    prompt: int
+    out_len: int
+    generated: int = 0
+    prompt_eff: int = 0      # tokens to prefill at the latest admission
+    prefilled: int = 0       # of prompt_eff written so far
+    ready: bool = False      # prompt fully written in an earlier step
+
+    def finished(self) -> bool:
+        return self.generated >= self.out_len
+
+
+@dataclass
+class StepRecord:
+    step: int
+    finished: list = field(default_factory=list)
+    arrived: list = field(default_factory=list)
+    admitted: list = field(default_factory=list)
+    prefill: list = field(default_factory=list)      # (rid, start, count, slots)
+    preempted: list = field(default_factory=list)
+    decode: list = field(default_factory=list)       # (rid, position, slot, cow)
+
+
+class SchedulerModel:
+    def __init__(self, num_blocks: int, block_size: int, chunk: int, initial_free_order=None):
+        self.alloc = AllocatorModel(num_blocks, block_size, initial_free_order)
+        self.B = block_size
+        self.chunk = chunk
+        self.waiting: deque[Request] = deque()
+        self.running: list[Request] = []
+        self.next_rid = 0
+
+    def step(self, n: int, arrivals) -> StepRecord:
+        """One iteration; `arrivals` is a list of (prompt, out_len)."""
+        rec = StepRecord(n)
+        # 1. finished requests give their pages back
+        for r in list(self.running):
+            if r.finished():
+                self.alloc.release(r.rid)
+                self.running.remove(r)
+                rec.finished.append(r.rid)
+        # 2a. new requests queue up behind the waiting ones
+        for prompt, out_len in arrivals:
+            r = Request(self.next_rid, int(prompt), int(out_len))
+            r.prompt_eff = r.prompt
+            self.next_rid += 1
+            self.waiting.append(r)
+            rec.arrived.append(r.rid)
+        # 2b. admit first come, first served while the whole prompt fits
+        while self.waiting:
+            r = self.waiting[0]
+            if -(-r.prompt_eff // self.B) > self.alloc.num_free():
+                break
+            self.alloc.add(r.rid, r.prompt_eff)
+            r.prefilled = 0
+            r.ready = False
+            self.running.append(r)
+            self.waiting.popleft()
+            rec.admitted.append(r.rid)
+        # 3a. prompts are written one chunk per request per step
+        decoders = [r for r in self.running if r.ready]
+        for r in self.running:
+            if r.prefilled < r.prompt_eff:
+                c = min(self.chunk, r.prompt_eff - r.prefilled)
+                rec.prefill.append((r.rid, r.prefilled, c,
+                                    self.alloc.slots(r.rid, r.prefilled, c)))
+                r.prefilled += c
+        # 3b. every decoding request appends one token (preempting when out of blocks)
+        for r in decoders:
+            while r in self.running:
+                try:
+                    slot, cow = self.alloc.append(r.rid)
+                except OutOfBlocks:
+                    victim = self.running[-1]
+                    self.alloc.release(victim.rid)
+                    self.running.remove(victim)
+                    victim.prompt_eff = victim.prompt + victim.generated
+                    victim.prefilled = 0
+                    victim.ready = False
+                    self.waiting.appendleft(victim)
+                    rec.preempted.append(victim.rid)
+                    continue
+                rec.decode.append((r.rid, self.alloc.length(r.rid) - 1, slot, cow))
+                r.generated += 1
+                break
+        # a prompt written this step decodes from the next one
+        for r in self.running:
+            if not r.ready and r.prefilled == r.prompt_eff:
+                r.ready = True
+        return rec

@@ -129,6 +129,12 @@ CONFIGS = {
         seed=6, dtype="bf16", num_q_heads=40, num_kv_heads=40, head_dim=128, block_size=16,
         num_blocks=50000, steps=200, arrival_mean=8.0, prompt_lo=32, prompt_hi=1024,
         out_p=0.01, out_lo=10, out_hi=500, chunk=512),
+    # small trace for GPU parity tests: same loop, a pool small enough to preempt
+    "trace_small": TraceConfig(
+        name="trace_small", title="continuous-batching trace, 48 steps, small pool, bf16",
+        seed=16, dtype="bf16", num_q_heads=8, num_kv_heads=4, head_dim=128, block_size=16,
+        num_blocks=160, steps=48, arrival_mean=2.0, prompt_lo=8, prompt_hi=300,
+        out_p=0.08, out_lo=2, out_hi=40, chunk=64),
 }
 
 

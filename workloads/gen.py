@@ -85,3 +85,42 @@ def context_lens_loguniform(seed: int, num_seqs: int, lo: int, hi: int) -> np.nd
 def pool_permutation(seed: int, num_blocks: int) -> np.ndarray:
     """A seeded permutation of the physical block IDs 0..N-1 (int32)."""
     return stream(seed, TAG_PERM).permutation(num_blocks).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------- serving trace
+
+TAG_TRACE_KV = 7   # keys/values of one token of one request of a serving trace
+TAG_TRACE_Q = 8    # query of one decode step of one request of a serving trace
+
+
+def trace_arrivals(seed: int, step: int, mean: float, prompt_lo: int, prompt_hi: int,
+                   out_p: float, out_lo: int, out_hi: int):
+    """Requests arriving at one step of a serving trace: Poisson(mean) of them, each
+    with a prompt length uniform on [prompt_lo, prompt_hi] and an output length
+    geometric(out_p) clipped to [out_lo, out_hi].  Returns (prompts, outputs)."""
+    rng = stream(seed, TAG_TRACE, step)
+    count = int(rng.poisson(mean))
+    prompts = rng.integers(prompt_lo, prompt_hi + 1, count)
+    outs = np.clip(rng.geometric(out_p, count), out_lo, out_hi)
+    return prompts.astype(np.int64), outs.astype(np.int64)
+
+
+def trace_token_kv(seed: int, req: int, positions, num_kv_heads: int, head_dim: int,
+                   dtype: str):
+    """Keys and values of tokens `positions` of request `req`: two [len, Hkv, D].
+
+    Each token's values depend only on (seed, req, position), so a request that is
+    preempted and prefilled again rewrites exactly the same bits."""
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1)
+    k = np.empty((len(positions), num_kv_heads, head_dim), dtype=np.float32 if dtype == "f32" else np.uint16)
+    v = np.empty_like(k)
+    for i, p in enumerate(positions.tolist()):
+        kv = draw_values(stream(seed, TAG_TRACE_KV, req, p), (2, num_kv_heads, head_dim), dtype)
+        k[i], v[i] = kv[0], kv[1]
+    return k, v
+
+
+def trace_query(seed: int, req: int, position: int, num_q_heads: int, head_dim: int,
+                dtype: str) -> np.ndarray:
+    """Query [Hq, D] of request `req` at the decode step that writes `position`."""
+    return draw_values(stream(seed, TAG_TRACE_Q, req, position), (num_q_heads, head_dim), dtype)
