@@ -17,6 +17,7 @@ and the CPU oracle timed on a sample of the same batch.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -391,7 +392,10 @@ def main():
         # a2: the step's metadata into a pinned ring slot the write kernel reads in place
         r = n % R
         if ring_ev[r] is not None:
-            ring_ev[r].synchronize()
+            # poll rather than block: a blocking wait may sleep the thread, and a late
+            # wake-up leaves the GPU without work
+            while not ring_ev[r].query():
+                pass
         ps, pc, pu, pp = (x.numpy() for x in views(pin[r]))
         ps[:] = slots
         pc[:] = ctx_now
@@ -428,6 +432,12 @@ def main():
             host.append((h1 - h0, time.perf_counter() - h0))
 
     ev = {"timed": [], "profile": []}
+    # A full collection of the interpreter's heap (hundreds of thousands of objects
+    # once torch is imported) stalls the host for tens of milliseconds and leaves the
+    # GPU without work; settle the heap now and keep the collector off while stepping.
+    gc.collect()
+    gc.freeze()
+    gc.disable()
     for n in range(warm):
         step(n, "warm")
     torch.cuda.synchronize()
@@ -443,6 +453,7 @@ def main():
     for n in range(warm + steps, total_steps):
         step(n, "profile")
     torch.cuda.synchronize()
+    gc.enable()
 
     tok = np.array([e[4] for e in ev["timed"]], dtype=np.float64)
     kv_bytes = tok * kv_per_tok
@@ -483,6 +494,7 @@ def main():
         },
         "host_bookkeeping_us_median": round(float(np.median([h[0] for h in host])) * 1e6, 2),
         "host_step_us_median": round(float(np.median([h[1] for h in host])) * 1e6, 2),
+        "host_step_us_max": round(float(np.max([h[1] for h in host])) * 1e6, 2),
         "roofline": {
             "kernel": "decode_pass1",
             "bound": "hbm",
@@ -493,6 +505,7 @@ def main():
             "traffic": measured_traffic(cfg.name),
             "pass1_us_mean": round(float(t_p1.mean()) * 1e6, 2),
             "pass1_us_median": round(float(np.median(t_p1)) * 1e6, 2),
+            "pass1_us_max": round(float(np.max(t_p1)) * 1e6, 2),
             "algorithmic_bytes_per_launch": int(np.median(kv_bytes)),
         },
     }
