@@ -74,7 +74,8 @@ def copy_calibration(mib: int):
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_397_amd", "csrc", "kernels_decode.hip")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_397_amd", "csrc", f)
+                  for f in ("kernels_decode.hip", "kernels_common.h")]
 
 
 def measured_traffic(config_name: str):
@@ -90,7 +91,7 @@ def measured_traffic(config_name: str):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             fields[k.strip()] = v.strip()
-    digest = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in DECODE_SOURCES)).hexdigest()
     if fields.get("kernel_source_sha256") != digest:
         return None
     return int(fields["traffic_bytes_per_launch"])

@@ -228,6 +228,41 @@ pa_status pa_paged_attn_decode_merge(const pa_cache_desc* desc, void* out, const
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked-prefill attention over the paged cache.
+ *
+ * The prompt is processed in one pass before decoding ([P1] section 2), long
+ * prompts a chunk at a time; generation is autoregressive, so a prompt token
+ * attends to itself and to every earlier token ([P1] section 2.1).  Sequence s
+ * brings c_s = query_start[s+1] - query_start[s] query rows (its chunk) and holds
+ * L_s = context_lens[s] >= c_s tokens in the cache, the chunk's own keys and
+ * values last (write them first with pa_reshape_and_cache).  Chunk token i sits
+ * at position L_s - c_s + i:
+ *   out[row, j, :] = sum_{p <= L_s - c_s + i} softmax_p(scale * <q[row, j], K_p>) V_p
+ * with row = query_start[s] + i, query head j reading KV head j / G.
+ *
+ *   out, q         device, [num_tokens, Hq, D] row-major, bf16, 16-B aligned
+ *   block_tables   device, [num_seqs, max_blocks_per_seq] int32 (as in decode)
+ *   query_start    device, [num_seqs + 1] int32, non-decreasing, 0 <= values
+ *                  <= num_tokens; sequences with c_s = 0 are skipped
+ *   context_lens   device, [num_seqs] int32, clamped to [0, max_blocks_per_seq * B]
+ *   max_query_len  host; every c_s must be <= it (it sizes the grid: rows past
+ *                  it may be left unwritten)
+ * Rows of a chunk longer than its cache (positions below 0) are written as
+ * zeros; rows whose query_start entries are out of range are not written.
+ * Block IDs outside [0, N) in a column that is read are replaced by 0.
+ * Supported: bf16 with G in {1, 2, 4, 8, 16} and D in {64, 128}
+ * (PA_ERR_UNSUPPORTED otherwise).  Accumulation is fp32, P is rounded to bf16
+ * before the PV product, and outputs are rounded nearest-even.  No workspace.
+ */
+pa_status pa_paged_attn_prefill(const pa_cache_desc* desc, void* out, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* query_start,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_tokens, int32_t num_q_heads,
+                                int32_t max_blocks_per_seq, int32_t max_query_len, float scale,
+                                void* stream);
+
+/*
  * Host block allocator ("block manager", [P1] section 2.2; sample structure in
  * [P3] section 2.2).  Host memory only; not thread-safe; one instance per
  * cache.  Semantics:

@@ -53,6 +53,8 @@ SIGNATURES = {
                                              c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_vp]),
     "pa_paged_attn_decode_merge": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                            c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_vp]),
+    "pa_paged_attn_prefill": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                      c_i32, c_i32, c_i32, c_i32, c_f32, c_vp]),
     "pa_alloc_create": (c_i32, [c_i32, c_i32, c_vp, ctypes.POINTER(c_vp)]),
     "pa_alloc_destroy": (None, [c_vp]),
     "pa_alloc_num_free": (c_i32, [c_vp]),

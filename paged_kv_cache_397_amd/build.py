@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedkv.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "allocator.cpp", "kernels_cache.hip", "kernels_decode.hip"]
+SOURCES = ["api.cpp", "allocator.cpp", "kernels_cache.hip", "kernels_decode.hip",
+           "kernels_prefill.hip"]
 ARCH = "gfx950"
 
 

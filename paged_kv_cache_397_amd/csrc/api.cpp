@@ -1,6 +1,6 @@
 // C ABI of libpagedkv: argument validation and kernel launches.  The kernels
-// live in kernels_cache.hip and kernels_decode.hip; the host allocator in
-// allocator.cpp.  No entry point allocates device memory.
+// live in kernels_cache.hip, kernels_decode.hip and kernels_prefill.hip; the host
+// allocator in allocator.cpp.  No entry point allocates device memory.
 
 #include <atomic>
 #include <cmath>
@@ -291,6 +291,59 @@ pa_status pa_paged_attn_decode_merge(const pa_cache_desc* d, void* out, const vo
     return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                        num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
                        workspace_bytes, stream, 2);
+}
+
+pa_status pa_paged_attn_prefill(const pa_cache_desc* d, void* out, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* query_start,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_tokens, int32_t num_q_heads,
+                                int32_t max_blocks_per_seq, int32_t max_query_len, float scale,
+                                void* stream) {
+    pa_status st = check_desc(d);
+    if (st != PA_OK) return st;
+    if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 ||
+        max_query_len < 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_q_heads % d->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+    const int32_t group = num_q_heads / d->num_kv_heads;
+    if (d->dtype != PA_DTYPE_BF16 || 16 % group != 0) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+    if (max_blocks_per_seq == 0) return PA_ERR_INVALID_ARG;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(query_start, 4) || !aligned(context_lens, 4))
+        return PA_ERR_INVALID_ARG;
+    const int32_t tpb = d->block_size / pkv::kTile;
+    // int32 in the kernel: cache tile indices, positions, and the workgroup count
+    // (at most num_seqs * Hkv * (max_query_len / 4 + 1) rounded up to 8)
+    if (static_cast<double>(d->num_blocks) * d->num_kv_heads * tpb >= 2147483647.0 ||
+        static_cast<double>(max_blocks_per_seq) * d->block_size >= 2147483647.0 ||
+        static_cast<double>(num_seqs) * d->num_kv_heads * (max_query_len / 4.0 + 2) >=
+            2147483647.0)
+        return PA_ERR_UNSUPPORTED;
+    pkv::PrefillArgs a;
+    a.q = q;
+    a.out = out;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.query_start = query_start;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = d->num_kv_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.tiles_per_block = tpb;
+    a.num_blocks = d->num_blocks;
+    a.qgroups = 0;
+    a.num_groups = 0;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    return from_hip(pkv::launch_prefill(d->head_dim, group, max_query_len, a,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

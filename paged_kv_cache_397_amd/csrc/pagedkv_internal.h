@@ -33,6 +33,27 @@ struct DecodeArgs {
     float scale_log2e;          // scale * log2(e): scores are kept in base-2 units
 };
 
+// Everything the chunked-prefill kernel needs; passed by value.
+struct PrefillArgs {
+    const void* q;                // [T, Hq, D]
+    void* out;                    // [T, Hq, D]
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;  // [S, max_blocks]
+    const int32_t* query_start;   // [S + 1]
+    const int32_t* context_lens;  // [S]
+    int32_t num_seqs;
+    int32_t num_tokens;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t max_blocks;
+    int32_t tiles_per_block;
+    int32_t num_blocks;
+    int32_t qgroups;              // workgroups per (sequence, KV head)
+    int32_t num_groups;           // num_seqs * num_kv_heads * qgroups
+    float scale_log2e;
+};
+
 constexpr int kRecInts = 8;  // per-unit record: row, seq, seq_begin, seq_end, tiles_per_unit
 
 // Floats of one partial-result record: heads_per_row * (D accumulators + max + sum).
@@ -57,6 +78,9 @@ hipError_t launch_update_block_tables(int32_t* tables, int rows, int cols, const
                                       int n, hipStream_t stream);
 // passes: bit 0 = pass 1 (tiles -> outputs / partial records), bit 1 = pass 2 (merge).
 // Returns hipErrorInvalidValue for an uncompiled (dtype, head_dim, group) combination.
+// Chunked-prefill attention (bf16, D in {64, 128}, G in {1, 2, 4, 8, 16}).
+hipError_t launch_prefill(int head_dim, int group, int max_query_len, PrefillArgs& a,
+                          hipStream_t stream);
 hipError_t launch_decode(int dtype, int head_dim, bool use_group_kernel, const DecodeArgs& a,
                          int passes, hipStream_t stream);
 

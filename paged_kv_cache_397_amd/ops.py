@@ -216,6 +216,38 @@ def paged_attn_decode_merge(spec: CacheSpec, out, q, k_cache, v_cache, block_tab
                    context_lens, scale, num_units, workspace, stream)
 
 
+def paged_attn_prefill(spec: CacheSpec, out, q, k_cache, v_cache, block_tables, query_start,
+                       context_lens, scale: float | None = None, max_query_len: int | None = None,
+                       stream=None):
+    """Chunked-prefill attention: rows query_start[s] .. query_start[s+1]-1 of q are the
+    last tokens of sequence s's cache (context_lens[s] tokens, the chunk included), and
+    each attends causally to its own position and every earlier one.
+
+    query_start and context_lens are int32 GPU tensors.  max_query_len bounds every
+    chunk length; when it is None it is read from query_start (a device-to-host copy,
+    which synchronises: pass it in a serving loop)."""
+    T, Hq, D = q.shape
+    if D != spec.head_dim or tuple(out.shape) != (T, Hq, D):
+        raise ValueError("q and out must be [T, Hq, D]")
+    S = context_lens.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.numel() != S + 1:
+        raise ValueError("block_tables must be [S, maxB], query_start [S + 1], context_lens [S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if S else 0
+    st = N.lib().pa_paged_attn_prefill(
+        ctypes.byref(spec.desc()), _dev(out, "out", spec.torch_dtype),
+        _dev(q, "q", spec.torch_dtype), _dev(k_cache, "k_cache", spec.torch_dtype),
+        _dev(v_cache, "v_cache", spec.torch_dtype),
+        _dev(block_tables, "block_tables", torch.int32),
+        _dev(query_start, "query_start", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, T, Hq, block_tables.shape[1],
+        int(max_query_len), float(scale), _stream(stream))
+    N.check(st, "pa_paged_attn_prefill")
+    return out
+
+
 class BoundCall:
     """A library call with every argument converted once, for tight serving loops:
     calling it costs one foreign-function call and a status check.  The buffers it

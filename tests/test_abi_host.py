@@ -103,3 +103,21 @@ def test_cache_write_host_validation():
     assert lib.pa_copy_blocks(ctypes.byref(d), None, FAKE, FAKE, 2, None) == N.PA_ERR_INVALID_ARG
     assert lib.pa_update_block_tables(FAKE, 4, 4, FAKE, 0, None) == N.PA_OK
     assert lib.pa_update_block_tables(None, 4, 4, FAKE, 1, None) == N.PA_ERR_INVALID_ARG
+
+
+def test_prefill_argument_checks_without_a_gpu():
+    """Rejections happen before any device work, so they run on the CPU."""
+    lib = N.lib()
+    S = N.PA_ERR_UNSUPPORTED
+    f32 = N.CacheDesc(64, 16, 2, 64, 0)
+    bf16 = N.CacheDesc(64, 16, 2, 64, 1)
+    args = lambda d, Hq, T=4, mql=4: (ctypes.byref(d), None, None, None, None, None, None, None,
+                                      1, T, Hq, 4, mql, 0.125, None)
+    assert lib.pa_paged_attn_prefill(*args(f32, 4)) == S            # no fp32 prefill kernel
+    assert lib.pa_paged_attn_prefill(*args(bf16, 6)) == S           # G = 3 does not divide 16
+    assert lib.pa_paged_attn_prefill(*args(bf16, 64)) == S          # G = 32
+    assert lib.pa_paged_attn_prefill(*args(bf16, 5)) == N.PA_ERR_INVALID_ARG  # Hq % Hkv != 0
+    assert lib.pa_paged_attn_prefill(*args(bf16, 4, T=-1)) == N.PA_ERR_INVALID_ARG
+    assert lib.pa_paged_attn_prefill(*args(bf16, 4, mql=-1)) == N.PA_ERR_INVALID_ARG
+    assert lib.pa_paged_attn_prefill(*args(bf16, 4, T=0)) == N.PA_OK  # nothing to do
+    assert lib.pa_paged_attn_prefill(*args(bf16, 4)) == N.PA_ERR_INVALID_ARG  # null pointers
