@@ -29,6 +29,7 @@ import numpy as np
 
 METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + µs/step, batch 256"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def log(msg):
@@ -42,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gqa_b256",
                     choices=["gqa_b256", "llama2_7b_b64", "shared_prefix_b16", "shared_prefix_b32",
-                             "trace_13b"])
+                             "trace_13b", "prefill_13b", "prefill_gqa"])
     ap.add_argument("--units", type=int, default=0, help="decode work units (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -78,12 +79,18 @@ DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_397_amd", "csrc", f)
                   for f in ("kernels_decode.hip", "kernels_common.h")]
 
 
-def measured_traffic(config_name: str):
-    """HBM bytes per launch of the decode kernel from the committed counter summary
+PREFILL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_397_amd", "csrc", f)
+                   for f in ("kernels_prefill.hip", "kernels_common.h")]
+
+
+def measured_traffic(config_name: str, kind: str = "decode", sources=None):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
     (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or
     None when there is none for this workload or the kernel source has changed since."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"decode_{config_name}_traffic.txt")
+    sources = DECODE_SOURCES if sources is None else sources
+    stem = config_name if config_name.startswith(kind) else f"{kind}_{config_name}"
+    path = os.path.join(ROOT, "profiles", f"{stem}_traffic.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -91,7 +98,7 @@ def measured_traffic(config_name: str):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             fields[k.strip()] = v.strip()
-    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in DECODE_SOURCES)).hexdigest()
+    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in sources)).hexdigest()
     if fields.get("kernel_source_sha256") != digest:
         return None
     return int(fields["traffic_bytes_per_launch"])
@@ -264,6 +271,139 @@ def spec_elem_bytes(dtype: str) -> int:
     return 4 if dtype == "f32" else 2
 
 
+def prefill_flops(offsets, chunk, num_q_heads, head_dim):
+    """Algorithmic flops of causal chunk attention: a token at position p attends to
+    p + 1 keys, 2 D flops each for QK^T and for PV, per query head."""
+    keys = sum(int(o) * chunk + chunk * (chunk + 1) // 2 for o in offsets)
+    return 4.0 * head_dim * num_q_heads * keys
+
+
+def cpu_baseline_prefill(cfg, offsets, seconds):
+    """Time the fp64 oracle (as it stands) on the first 32 rows of each of the first
+    two chunks, with seeded data of the same shapes."""
+    from oracle.attention import prefill_attention
+    from oracle.layout import to_float64
+    from workloads import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    rows = 32
+    work = []
+    for s in range(2):
+        L = int(offsets[s]) + cfg.chunk
+        K, V = gen.seq_kv(cfg.seed, s, L, cfg.num_kv_heads, cfg.head_dim, cfg.dtype)
+        q = gen.q_values(cfg.seed, 1 + s, rows, cfg.num_q_heads, cfg.head_dim, cfg.dtype)
+        work.append((to_float64(q, cfg.dtype), to_float64(K, cfg.dtype), to_float64(V, cfg.dtype),
+                     int(offsets[s])))
+    flops = sum(4.0 * cfg.head_dim * cfg.num_q_heads * (rows * o + rows * (rows + 1) // 2)
+                for _, _, _, o in work)
+    times = []
+    t_end = time.perf_counter() + seconds
+    while not times or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        for q, K, V, o in work:
+            prefill_attention(q, K[:o + rows], V[:o + rows], cfg.scale, o)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle on the first {rows} rows of chunks 0 and 1 "
+                       f"(offsets {int(offsets[0])}, {int(offsets[1])}), median of {len(times)} runs"),
+            "seconds_per_run": t}
+
+
+def run_prefill(args):
+    """Chunked-prefill attention: every sequence's cache holds its offset plus its
+    chunk (written beforehand); one call attends every chunk token causally.  A step
+    is one call over the whole batch of chunks, inputs resident in HBM."""
+    import torch
+    from paged_kv_cache_397_amd import ops, _native
+    from paged_kv_cache_397_amd.batch import PagedKVCache
+    from workloads import CONFIGS
+
+    _native.lib()
+    cfg = CONFIGS[args.config]
+    S, Hq, Hkv, D, B, c = (cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                           cfg.block_size, cfg.chunk)
+    spec = ops.CacheSpec(cfg.num_blocks, B, Hkv, D, cfg.dtype)
+    offsets = cfg.offsets()
+    L = (offsets + c).astype(np.int32)
+    cache = PagedKVCache(spec, cfg.pool_order(), fill=0.0)
+    for i in range(S):
+        cache.alloc.add(i, int(L[i]))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    # values do not change the timing; parity of this kernel is a test
+    cache.k.copy_(torch.randn(cache.k.shape, generator=g, device="cuda", dtype=torch.float32))
+    cache.v.copy_(torch.randn(cache.v.shape, generator=g, device="cuda", dtype=torch.float32))
+    tables, ctx, _, _ = cache.metadata(range(S))
+    T = S * c
+    q = torch.randn(T, Hq, D, generator=g, device="cuda", dtype=torch.float32).to(spec.torch_dtype)
+    out = torch.empty_like(q)
+    qs = torch.arange(0, T + 1, c, dtype=torch.int32, device="cuda")
+    ctx_dev = torch.from_numpy(L).cuda()
+    stream = torch.cuda.current_stream()
+    call = lambda: ops.paged_attn_prefill(spec, out, q, cache.k, cache.v, tables, qs, ctx_dev,
+                                          cfg.scale, max_query_len=c, stream=stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    per = []
+    for _ in range(10):  # per-launch durations, untimed
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) * 1e-3)
+    flops = prefill_flops(offsets, c, Hq, D)
+    kv_bytes = float(L.sum()) * 2 * Hkv * D * spec_elem_bytes(cfg.dtype)
+    tflops = flops / dev_s / 1e12
+    result = {
+        "metric": "chunked-prefill attention TFLOP/s (causal, paged K/V)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dev_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.title}", "seqs": S, "chunk": c,
+                   "offsets": offsets.tolist(), "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                   "block_size": B, "seed": cfg.seed},
+        "wall_ms_timed": round(wall * 1e3, 3),
+        "launch_us": {"median": round(float(np.median(per)) * 1e6, 2),
+                      "min": round(float(np.min(per)) * 1e6, 2)},
+        "flops_per_step": flops,
+        "unique_kv_bytes_per_step": kv_bytes,
+        "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(cfg.name, "prefill", PREFILL_SOURCES),
+                     "unique_kv_gbps": round(kv_bytes / dev_s / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on the host)")
+        result["cpu_baseline"] = cpu_baseline_prefill(cfg, offsets, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -276,6 +416,9 @@ def main():
         return
     if args.config == "trace_13b":
         run_trace(args)
+        return
+    if args.config.startswith("prefill"):
+        run_prefill(args)
         return
     import torch
     from paged_kv_cache_397_amd import ops, _native

@@ -86,15 +86,20 @@ __device__ __forceinline__ void store_out<uint32_t>(uint32_t* p, float x) {
 // Token k of tile t is visible to lane's column when 16 t + k < lim (lim may differ
 // per lane: the causal limit of a prefill row).  Value rows of tokens at or past
 // vlim (the sequence length) are zeroed first: their slots may hold anything, and
-// a zero weight times a NaN would still poison the sum.  Every column must see at
-// least one token of the first tile it folds, so that its running max is finite.
+// a zero weight times a NaN would still poison the sum; vlim must be uniform over
+// the wave.  Every column must see at least one token of the first tile it folds, so
+// that its running max is finite.
 template <int D>
 struct GroupAcc {
     float m, l;
     f32x4 acc[D / 16];
 };
 
-template <int D>
+// kLazy: skip the accumulator rescale when no factor changed and mask V only on the
+// sequence's last tile (bit-identical results).  It saves VALU work where the tile
+// math bounds the kernel (prefill); the decode loop, bound by HBM, keeps the
+// straight-line form, which needs fewer registers there.
+template <int D, bool kLazy>
 __device__ __forceinline__ void group_tile(GroupAcc<D>& st, const u32x4 (&q)[D / 32],
                                            const u32x4* kb, const u32x4* vb, int t, int lim,
                                            int vlim, float scale_log2e, int lane) {
@@ -126,26 +131,58 @@ __device__ __forceinline__ void group_tile(GroupAcc<D>& st, const u32x4 (&q)[D /
     const s16x4 pB = __builtin_bit_cast(
         s16x4, (unsigned __attribute__((ext_vector_type(2)))){pb[0] | (pb[1] << 16),
                                                               pb[2] | (pb[3] << 16)});
+    if constexpr (!kLazy) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) st.acc[g] *= alpha;
-    const bool last = t * kTile + kTile > vlim;
-    uint32_t mask01 = 0xffffffffu, mask23 = 0xffffffffu;
-    if (last) {
-        const int nv = vlim - tok0;
-        mask01 = (nv > 0 ? 0x0000ffffu : 0u) | (nv > 1 ? 0xffff0000u : 0u);
-        mask23 = (nv > 2 ? 0x0000ffffu : 0u) | (nv > 3 ? 0xffff0000u : 0u);
-    }
-#pragma unroll
-    for (int mm = 0; mm < NL; ++mm) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const unsigned w0 = vb[mm][2 * e] & mask01;
-            const unsigned w1 = vb[mm][2 * e + 1] & mask23;
-            const s16x4 vA =
-                __builtin_bit_cast(s16x4, (unsigned __attribute__((ext_vector_type(2)))){w0, w1});
-            st.acc[2 * mm + e] =
-                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pB, st.acc[2 * mm + e], 0, 0, 0);
+        for (int g = 0; g < NG; ++g) st.acc[g] *= alpha;
+        const bool last = t * kTile + kTile > vlim;
+        uint32_t mask01 = 0xffffffffu, mask23 = 0xffffffffu;
+        if (last) {
+            const int nv = vlim - tok0;
+            mask01 = (nv > 0 ? 0x0000ffffu : 0u) | (nv > 1 ? 0xffff0000u : 0u);
+            mask23 = (nv > 2 ? 0x0000ffffu : 0u) | (nv > 3 ? 0xffff0000u : 0u);
         }
+#pragma unroll
+        for (int mm = 0; mm < NL; ++mm) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const unsigned w0 = vb[mm][2 * e] & mask01;
+                const unsigned w1 = vb[mm][2 * e + 1] & mask23;
+                const s16x4 vA = __builtin_bit_cast(
+                    s16x4, (unsigned __attribute__((ext_vector_type(2)))){w0, w1});
+                st.acc[2 * mm + e] =
+                    __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pB, st.acc[2 * mm + e], 0, 0, 0);
+            }
+        }
+        return;
+    }
+    // The accumulators sit in the matrix cores' registers, so a rescale costs a read,
+    // a multiply and a write per element.  Once the running maxima settle, most tiles
+    // leave every factor at exactly 1 (2^0), and multiplying by 1 changes no bit:
+    // skip the rescale then.
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) st.acc[g] *= alpha;
+    }
+    auto pv = [&](uint32_t mask01, uint32_t mask23) {
+#pragma unroll
+        for (int mm = 0; mm < NL; ++mm) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const unsigned w0 = vb[mm][2 * e] & mask01;
+                const unsigned w1 = vb[mm][2 * e + 1] & mask23;
+                const s16x4 vA = __builtin_bit_cast(
+                    s16x4, (unsigned __attribute__((ext_vector_type(2)))){w0, w1});
+                st.acc[2 * mm + e] =
+                    __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pB, st.acc[2 * mm + e], 0, 0, 0);
+            }
+        }
+    };
+    if (t * kTile + kTile > vlim) {  // the sequence's last tile (vlim is uniform)
+        const int nv = vlim - tok0;
+        pv((nv > 0 ? 0x0000ffffu : 0u) | (nv > 1 ? 0xffff0000u : 0u),
+           (nv > 2 ? 0x0000ffffu : 0u) | (nv > 3 ? 0xffff0000u : 0u));
+    } else {
+        pv(0xffffffffu, 0xffffffffu);
     }
 }
 

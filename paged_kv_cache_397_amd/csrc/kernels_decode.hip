@@ -255,7 +255,7 @@ struct GroupPath {
     static __device__ __forceinline__ void tile(const DecodeArgs& a, Acc& st, const Q& q,
                                                 const u32x4* kb, const u32x4* vb, int t, int ctx,
                                                 int lane) {
-        group_tile<D>(st, q.v, kb, vb, t, ctx, ctx, a.scale_log2e, lane);
+        group_tile<D, false>(st, q.v, kb, vb, t, ctx, ctx, a.scale_log2e, lane);
     }
 
     static __device__ __forceinline__ void finish(const DecodeArgs& a, Acc& st, int row, int seq,

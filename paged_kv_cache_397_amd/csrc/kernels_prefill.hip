@@ -133,11 +133,11 @@ __global__ __launch_bounds__(kQBlocksPerGroup * kWave) void prefill_kernel(Prefi
     for (int t = 0; t < nt; t += 2) {
         wait_all_loads();
         if (t + 1 < nt) fetch(kb, vb, t + 1);
-        group_tile<D>(st, q, ka, va, t, lim, L, a.scale_log2e, lane);
+        group_tile<D, true>(st, q, ka, va, t, lim, L, a.scale_log2e, lane);
         if (t + 1 >= nt) break;
         wait_all_loads();
         if (t + 2 < nt) fetch(ka, va, t + 2);
-        group_tile<D>(st, q, kb, vb, t + 1, lim, L, a.scale_log2e, lane);
+        group_tile<D, true>(st, q, kb, vb, t + 1, lim, L, a.scale_log2e, lane);
     }
 
     float l = st.l;

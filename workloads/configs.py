@@ -101,6 +101,39 @@ class TraceConfig:
         return self.num_q_heads // self.num_kv_heads
 
 
+@dataclass(frozen=True)
+class PrefillConfig:
+    """Prompt chunks at the end of partly filled caches, as a serving step prefills them."""
+    name: str
+    title: str
+    seed: int
+    dtype: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    chunk: int                    # tokens per chunk
+    offset_lo: int                # tokens already cached before the chunk: U[lo, hi]
+    offset_hi: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def offsets(self) -> np.ndarray:
+        return gen.stream(self.seed, gen.TAG_CTX).integers(
+            self.offset_lo, self.offset_hi + 1, self.num_seqs).astype(np.int32)
+
+    def pool_order(self) -> np.ndarray:
+        return gen.pool_permutation(self.seed, self.num_blocks)
+
+
 CONFIGS = {
     "tiny_f32": DecodeConfig(
         name="tiny_f32", title="tiny paged decode, fp32, 4 seqs, ctx {1,15,16,33}",
@@ -129,6 +162,14 @@ CONFIGS = {
         seed=6, dtype="bf16", num_q_heads=40, num_kv_heads=40, head_dim=128, block_size=16,
         num_blocks=50000, steps=200, arrival_mean=8.0, prompt_lo=32, prompt_hi=1024,
         out_p=0.01, out_lo=10, out_hi=500, chunk=512),
+    "prefill_13b": PrefillConfig(
+        name="prefill_13b", title="chunked prefill, 8 chunks of 512 after U[0,3584] cached tokens, "
+        "40x128 heads, bf16", seed=7, dtype="bf16", num_seqs=8, num_q_heads=40, num_kv_heads=40,
+        head_dim=128, block_size=16, num_blocks=4096, chunk=512, offset_lo=0, offset_hi=3584),
+    "prefill_gqa": PrefillConfig(
+        name="prefill_gqa", title="chunked prefill, 8 chunks of 512 after U[0,3584] cached tokens, "
+        "32q/8kv x 128, bf16", seed=8, dtype="bf16", num_seqs=8, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, block_size=16, num_blocks=4096, chunk=512, offset_lo=0, offset_hi=3584),
     # small trace for GPU parity tests: same loop, a pool small enough to preempt
     "trace_small": TraceConfig(
         name="trace_small", title="continuous-batching trace, 48 steps, small pool, bf16",
