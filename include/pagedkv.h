@@ -327,6 +327,39 @@ pa_status pa_batch_metadata(const pa_allocator* a, const int64_t* seqs, int32_t 
                             int32_t max_blocks_per_seq, int32_t* block_tables,
                             int32_t* context_lens);
 
+/*
+ * Prefix caching: prompts that open with the same tokens share those tokens'
+ * pages instead of computing them again ([P2] 优势 > 3. 支持共享; [P1] sections
+ * 3.4 and 5.2 item 4).  The pages give no mechanism; this one:
+ *   - a full block is identified by key_i = FNV-1a-64(le64(key_{i-1}) ||
+ *     le32(its B tokens)), key_{-1} = 0 (equal keys are taken as equal
+ *     prefixes; a 64-bit collision would share a wrong block);
+ *   - add_prefix(seq, tokens, n) admits a prompt of n tokens: its leading full
+ *     blocks whose keys are cached are reused (reference + 1; a cached block
+ *     with no holder leaves the free queue), never the block of token n - 1,
+ *     and the rest is taken from the queue as in add.  *num_cached_tokens =
+ *     reused blocks * B: those tokens' K/V are already in the cache.  OOM when
+ *     the queue, less the reused blocks in it, is short; nothing changes then;
+ *   - register_blocks(seq, tokens, n): tokens are the sequence's first n tokens
+ *     (n <= its length) and their K/V are written.  Each full block among them
+ *     is considered once per sequence, in order: it becomes the cached block
+ *     for its key unless that key is cached already (the duplicate stays
+ *     uncached).  A forked child inherits its parent's progress;
+ *   - a cached block whose last holder lets go joins the free queue's tail
+ *     like any block and stays findable; any allocation that takes it from
+ *     the head evicts it (its key is forgotten).
+ * Calls that pass no tokens (pa_seq_add, appends) never look blocks up.
+ */
+pa_status pa_seq_add_prefix(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                            int32_t num_tokens, int32_t* num_cached_tokens);
+pa_status pa_seq_register_blocks(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                                 int32_t num_tokens);
+/* Blocks looked up and reused by add_prefix so far, and blocks cached now. */
+pa_status pa_alloc_prefix_stats(const pa_allocator* a, int64_t* lookups, int64_t* hits,
+                                int32_t* cached_blocks);
+/* 1 and *key when the block is cached, 0 when not, -1 if out of range. */
+int32_t   pa_alloc_block_cached(const pa_allocator* a, int32_t block, uint64_t* key);
+
 #ifdef __cplusplus
 }
 #endif

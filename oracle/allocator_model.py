@@ -38,11 +38,57 @@ Pins: the worked examples above (``tests/golden/allocator_examples.json``);
 conservation (free + held = N; sum of reference counts = total table length);
 freeing everything restores the pool; brute force over every operation sequence
 of length <= 6 on a 4-block pool against these invariants.
+
+Prefix caching.  Requests whose prompts start with the same tokens (a shared
+system prompt) can share those tokens' cache pages instead of computing them
+again (hihuo.com page, 优势 > 3. 支持共享; ksqn.cn page, 3.4 and 5.2 item 4 on
+``--enable-prefix-caching``).  The pages give no mechanism; the readings here:
+
+* Only full blocks are shared.  A full block is identified by a chain hash over
+  its tokens and its predecessor's hash, so equal hashes mean equal prefixes (up
+  to 64-bit hash collisions): h_i = FNV-1a-64(le64(h_{i-1}) || le32(tokens of
+  block i)), h_{-1} = 0, FNV-1a-64 as published by its authors (offset basis
+  0xcbf29ce484222325, prime 0x100000001b3, xor then multiply per byte).
+* ``add_prefix`` reuses the longest run of cached blocks from the start of the
+  prompt, but never a block holding the prompt's last token (that token must be
+  computed to produce the next one); the rest is allocated as usual.  A reused
+  block with no holder leaves the free queue; all-or-nothing as ``add``.
+* ``register`` is called once a sequence's blocks hold written K/V; it considers
+  each full block once, in order: a block whose hash is not cached yet becomes
+  the cached block for it; a duplicate of a cached hash stays uncached.
+* A cached block whose last holder lets go joins the free queue's tail like any
+  other block and stays findable; it is evicted (its hash forgotten) only when
+  an allocation takes it from the head of the queue.  The FIFO queue is thereby
+  least-recently-freed-first.
+
+Prefix-cache pins: published FNV-1a-64 test vectors; a hand-worked run on a
+six-block pool (tests/test_prefix_cache.py); content safety over random runs
+(every reused block holds exactly the tokens the new prompt has at that place).
 """
 
 from __future__ import annotations
 
 from collections import deque
+
+
+FNV64_OFFSET = 0xCBF29CE484222325
+FNV64_PRIME = 0x100000001B3
+MASK64 = (1 << 64) - 1
+
+
+def fnv1a64(data: bytes) -> int:
+    """FNV-1a, 64 bits: for each byte, xor it in, then multiply by the prime."""
+    h = FNV64_OFFSET
+    for byte in data:
+        h = ((h ^ byte) * FNV64_PRIME) & MASK64
+    return h
+
+
+def chain_hash(parent: int, block_tokens) -> int:
+    """Identity of a full block: its tokens after its predecessor's identity."""
+    data = parent.to_bytes(8, "little") + b"".join(
+        (int(t) & 0xFFFFFFFF).to_bytes(4, "little") for t in block_tokens)
+    return fnv1a64(data)
 
 
 class AllocError(Exception):
@@ -74,6 +120,13 @@ class AllocatorModel:
         self.ref = [0] * num_blocks
         self.tables: dict[int, list[int]] = {}
         self.lengths: dict[int, int] = {}
+        # prefix cache: chain hash -> block, block -> chain hash, and per sequence
+        # (leading full blocks already considered, chain hash after them)
+        self.cached: dict[int, int] = {}
+        self.block_hash: dict[int, int] = {}
+        self.progress: dict[int, tuple[int, int]] = {}
+        self.lookups = 0
+        self.hits = 0
 
     # -- queries ---------------------------------------------------------------
     def num_free(self) -> int:
@@ -112,12 +165,69 @@ class AllocatorModel:
         need = -(-num_tokens // self.block_size)
         if need > len(self.free):
             raise OutOfBlocks(f"need {need} blocks, {len(self.free)} free")
-        blocks = [self.free.popleft() for _ in range(need)]
-        for b in blocks:
-            self.ref[b] = 1
+        blocks = [self._take() for _ in range(need)]
         self.tables[seq] = blocks
         self.lengths[seq] = num_tokens
+        self.progress[seq] = (0, 0)
         return list(blocks)
+
+    def add_prefix(self, seq: int, tokens) -> int:
+        """Admit a new sequence whose prompt is ``tokens``, reusing cached blocks
+        for the longest cached run of its leading full blocks.  Returns the number
+        of prompt tokens whose K/V are already in the cache."""
+        if seq in self.tables:
+            raise BadState(f"sequence {seq} already exists")
+        tokens = [int(t) for t in tokens]
+        n, B = len(tokens), self.block_size
+        eligible = (n - 1) // B if n > 0 else 0   # never the block of the last token
+        hits, h = [], 0
+        for i in range(eligible):
+            h = chain_hash(h, tokens[i * B:(i + 1) * B])
+            if h not in self.cached:
+                break
+            hits.append(self.cached[h])
+        need = -(-n // B) - len(hits)
+        idle = sum(1 for b in hits if self.ref[b] == 0)
+        if need > len(self.free) - idle:
+            raise OutOfBlocks(f"need {need} blocks, {len(self.free) - idle} free")
+        self.lookups += eligible
+        self.hits += len(hits)
+        for b in hits:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+        blocks = hits + [self._take() for _ in range(need)]
+        self.tables[seq] = blocks
+        self.lengths[seq] = n
+        self.progress[seq] = (len(hits), h if hits else 0)
+        return len(hits) * B
+
+    def register(self, seq: int, tokens) -> None:
+        """Offer the sequence's full blocks covered by ``tokens`` (its first
+        len(tokens) tokens, K/V written) to the prefix cache, each block once."""
+        self._need(seq)
+        tokens = [int(t) for t in tokens]
+        if len(tokens) > self.lengths[seq]:
+            raise BadArgument("more tokens than the sequence holds")
+        B = self.block_size
+        done, h = self.progress[seq]
+        table = self.tables[seq]
+        for i in range(done, len(tokens) // B):
+            h = chain_hash(h, tokens[i * B:(i + 1) * B])
+            b = table[i]
+            if b not in self.block_hash and h not in self.cached:
+                self.cached[h] = b
+                self.block_hash[b] = h
+            done = i + 1
+        self.progress[seq] = (done, h)
+
+    def _take(self) -> int:
+        """The head of the free queue for a new use; a cached block is evicted."""
+        b = self.free.popleft()
+        if b in self.block_hash:
+            del self.cached[self.block_hash.pop(b)]
+        self.ref[b] = 1
+        return b
 
     def append(self, seq: int):
         """Reserve the slot of the sequence's next token.
@@ -134,15 +244,13 @@ class AllocatorModel:
         if j == len(table):
             if not self.free:
                 raise OutOfBlocks("no free block for a new page")
-            nb = self.free.popleft()
-            self.ref[nb] = 1
+            nb = self._take()
             table.append(nb)
         elif self.ref[table[j]] > 1:
             if not self.free:
                 raise OutOfBlocks("no free block for copy-on-write")
             old = table[j]
-            nb = self.free.popleft()
-            self.ref[nb] = 1
+            nb = self._take()
             self.ref[old] -= 1
             table[j] = nb
             cow = (old, nb)
@@ -159,6 +267,7 @@ class AllocatorModel:
             self.ref[b] += 1
         self.tables[child] = t
         self.lengths[child] = self.lengths[parent]
+        self.progress[child] = self.progress[parent]
 
     def release(self, seq: int) -> None:
         """Drop the sequence; blocks whose count reaches zero join the free tail."""
@@ -169,6 +278,7 @@ class AllocatorModel:
                 self.free.append(b)
         del self.tables[seq]
         del self.lengths[seq]
+        del self.progress[seq]
 
     # -- helpers ---------------------------------------------------------------
     def _need(self, seq: int) -> None:
@@ -182,4 +292,5 @@ class AllocatorModel:
             "ref": list(self.ref),
             "tables": {s: list(t) for s, t in sorted(self.tables.items())},
             "lengths": dict(sorted(self.lengths.items())),
+            "cached": dict(sorted(self.block_hash.items())),
         }

@@ -70,6 +70,10 @@ SIGNATURES = {
     "pa_seq_info": (c_i32, [c_vp, c_i64, P_i32, P_i32]),
     "pa_seq_block_table": (c_i32, [c_vp, c_i64, c_vp, c_i32]),
     "pa_batch_metadata": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_vp]),
+    "pa_seq_add_prefix": (c_i32, [c_vp, c_i64, c_vp, c_i32, P_i32]),
+    "pa_seq_register_blocks": (c_i32, [c_vp, c_i64, c_vp, c_i32]),
+    "pa_alloc_prefix_stats": (c_i32, [c_vp, P_i64, P_i64, P_i32]),
+    "pa_alloc_block_cached": (c_i32, [c_vp, c_i32, ctypes.POINTER(ctypes.c_uint64)]),
 }
 
 _lib = None

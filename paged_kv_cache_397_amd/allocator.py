@@ -124,3 +124,36 @@ class BlockAllocator:
 
     def free(self, seq: int) -> None:
         N.check(self._lib.pa_seq_free(self._h, seq), "seq_free")
+
+    # -- prefix cache ---------------------------------------------------------
+    def add_prefix(self, seq: int, tokens) -> int:
+        """Admit a prompt, reusing cached full blocks of its opening; returns the
+        number of leading tokens whose K/V are already cached."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        cached = ctypes.c_int32()
+        N.check(self._lib.pa_seq_add_prefix(self._h, seq, _ptr(t), t.shape[0], ctypes.byref(cached)),
+                "seq_add_prefix")
+        return cached.value
+
+    def register(self, seq: int, tokens) -> None:
+        """Offer the full blocks covered by the sequence's first len(tokens) tokens
+        (their K/V written) to the prefix cache."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        N.check(self._lib.pa_seq_register_blocks(self._h, seq, _ptr(t), t.shape[0]),
+                "seq_register_blocks")
+
+    def prefix_stats(self):
+        """(blocks looked up, blocks reused, blocks cached now)."""
+        lk, ht, nc = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        N.check(self._lib.pa_alloc_prefix_stats(self._h, ctypes.byref(lk), ctypes.byref(ht),
+                                                ctypes.byref(nc)), "alloc_prefix_stats")
+        return lk.value, ht.value, nc.value
+
+    def cached_blocks(self) -> dict[int, int]:
+        """{block: key} for every cached block."""
+        key = ctypes.c_uint64()
+        out = {}
+        for b in range(self.num_blocks):
+            if self._lib.pa_alloc_block_cached(self._h, b, ctypes.byref(key)) == 1:
+                out[b] = key.value
+        return out

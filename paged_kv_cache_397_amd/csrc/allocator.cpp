@@ -11,27 +11,96 @@
 // counts and copy-on-write.  Every operation either succeeds or leaves the
 // state untouched.
 //
+// Prefix caching (same section; ksqn.cn page, 3.4 and 5.2 item 4): a full block
+// whose K/V are written can be offered to a cache keyed by a chain hash of its
+// tokens and its predecessor's key, so that a later prompt opening with the same
+// tokens takes those blocks instead of computing them again.  A cached block
+// without holders stays in the free queue, findable, until an allocation takes
+// it from the head (eviction).  Hits may leave the middle of the queue, so the
+// queue is a doubly linked list over block IDs.
+//
 // Plain C++17, no HIP: this file also builds with g++ alone.
 
 #include <cstdint>
 #include <cstring>
-#include <deque>
 #include <new>
 #include <unordered_map>
 #include <vector>
 
 #include "pagedkv.h"
 
+namespace {
+
+// FNV-1a, 64 bits, as published by its authors: xor each byte in, then multiply
+// by the prime.
+constexpr uint64_t kFnvOffset = 0xCBF29CE484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001B3ull;
+
+inline uint64_t fnv_byte(uint64_t h, uint8_t b) { return (h ^ b) * kFnvPrime; }
+
+// Key of a full block: its parent's key (8 bytes, little-endian) followed by its
+// tokens (4 bytes each, little-endian), hashed with FNV-1a-64.
+uint64_t chain_hash(uint64_t parent, const int32_t* tokens, int32_t n) {
+    uint64_t h = kFnvOffset;
+    for (int k = 0; k < 8; ++k) h = fnv_byte(h, static_cast<uint8_t>(parent >> (8 * k)));
+    for (int32_t i = 0; i < n; ++i) {
+        const uint32_t t = static_cast<uint32_t>(tokens[i]);
+        for (int k = 0; k < 4; ++k) h = fnv_byte(h, static_cast<uint8_t>(t >> (8 * k)));
+    }
+    return h;
+}
+
+}  // namespace
+
 struct pa_allocator {
     struct Seq {
         std::vector<int32_t> table;
         int32_t len = 0;
+        int32_t reg_done = 0;   // leading full blocks already offered to the prefix cache
+        uint64_t reg_hash = 0;  // chain key after them
     };
     int32_t num_blocks = 0;
     int32_t block_size = 0;
-    std::deque<int32_t> free_q;
+    // free queue (FIFO): a doubly linked list over block IDs, -1 terminated
+    std::vector<int32_t> next, prev;
+    std::vector<char> in_free;
+    int32_t head = -1, tail = -1, nfree = 0;
     std::vector<int32_t> ref;
     std::unordered_map<int64_t, Seq> seqs;
+    // prefix cache
+    std::unordered_map<uint64_t, int32_t> cached;  // key -> block
+    std::vector<uint64_t> key;                     // block -> key, when is_cached
+    std::vector<char> is_cached;
+    int64_t lookups = 0, hits = 0;
+
+    void push_back(int32_t b) {
+        prev[b] = tail;
+        next[b] = -1;
+        if (tail >= 0) next[tail] = b; else head = b;
+        tail = b;
+        in_free[b] = 1;
+        ++nfree;
+    }
+    void unlink(int32_t b) {
+        if (prev[b] >= 0) next[prev[b]] = next[b]; else head = next[b];
+        if (next[b] >= 0) prev[next[b]] = prev[b]; else tail = prev[b];
+        in_free[b] = 0;
+        --nfree;
+    }
+    // The head of the free queue for a new use; a cached block is evicted.
+    int32_t take() {
+        const int32_t b = head;
+        unlink(b);
+        if (is_cached[b]) {
+            cached.erase(key[b]);
+            is_cached[b] = 0;
+        }
+        ref[b] = 1;
+        return b;
+    }
+    void release_block(int32_t b) {
+        if (--ref[b] == 0) push_back(b);
+    }
 
     // Reserve the slot of seq's next token; see pa_seq_append.
     pa_status append(int64_t id, int64_t* slot, int32_t* cow_src, int32_t* cow_dst,
@@ -43,16 +112,12 @@ struct pa_allocator {
         const int32_t j = pos / block_size;
         int32_t src = -1, dst = -1, fresh = -1;
         if (j == static_cast<int32_t>(s.table.size())) {
-            if (free_q.empty()) return PA_ERR_OOM;
-            fresh = free_q.front();
-            free_q.pop_front();
-            ref[fresh] = 1;
+            if (nfree == 0) return PA_ERR_OOM;
+            fresh = take();
             s.table.push_back(fresh);
         } else if (ref[s.table[j]] > 1) {
-            if (free_q.empty()) return PA_ERR_OOM;
-            fresh = free_q.front();
-            free_q.pop_front();
-            ref[fresh] = 1;
+            if (nfree == 0) return PA_ERR_OOM;
+            fresh = take();
             src = s.table[j];
             dst = fresh;
             ref[src] -= 1;
@@ -79,19 +144,22 @@ pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
     a->num_blocks = num_blocks;
     a->block_size = block_size;
     a->ref.assign(num_blocks, 0);
+    a->next.assign(num_blocks, -1);
+    a->prev.assign(num_blocks, -1);
+    a->in_free.assign(num_blocks, 0);
+    a->key.assign(num_blocks, 0);
+    a->is_cached.assign(num_blocks, 0);
     if (initial_free_order) {
-        std::vector<char> seen(num_blocks, 0);
         for (int32_t k = 0; k < num_blocks; ++k) {
             const int32_t b = initial_free_order[k];
-            if (b < 0 || b >= num_blocks || seen[b]) {
+            if (b < 0 || b >= num_blocks || a->in_free[b]) {
                 delete a;
                 return PA_ERR_INVALID_ARG;
             }
-            seen[b] = 1;
-            a->free_q.push_back(b);
+            a->push_back(b);
         }
     } else {
-        for (int32_t b = 0; b < num_blocks; ++b) a->free_q.push_back(b);
+        for (int32_t b = 0; b < num_blocks; ++b) a->push_back(b);
     }
     *out = a;
     return PA_OK;
@@ -99,9 +167,7 @@ pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
 
 void pa_alloc_destroy(pa_allocator* a) { delete a; }
 
-int32_t pa_alloc_num_free(const pa_allocator* a) {
-    return a ? static_cast<int32_t>(a->free_q.size()) : -1;
-}
+int32_t pa_alloc_num_free(const pa_allocator* a) { return a ? a->nfree : -1; }
 
 int32_t pa_alloc_num_seqs(const pa_allocator* a) {
     return a ? static_cast<int32_t>(a->seqs.size()) : -1;
@@ -114,10 +180,9 @@ int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block) {
 
 pa_status pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n) {
     if (!a || !n || cap < 0 || (cap > 0 && !out)) return PA_ERR_INVALID_ARG;
-    const int32_t len = static_cast<int32_t>(a->free_q.size());
-    *n = len;
+    *n = a->nfree;
     int32_t k = 0;
-    for (auto it = a->free_q.begin(); it != a->free_q.end() && k < cap; ++it) out[k++] = *it;
+    for (int32_t b = a->head; b >= 0 && k < cap; b = a->next[b]) out[k++] = b;
     return PA_OK;
 }
 
@@ -125,18 +190,88 @@ pa_status pa_seq_add(pa_allocator* a, int64_t seq, int32_t num_tokens) {
     if (!a || num_tokens < 0) return PA_ERR_INVALID_ARG;
     if (a->seqs.count(seq)) return PA_ERR_STATE;
     const int64_t need = (static_cast<int64_t>(num_tokens) + a->block_size - 1) / a->block_size;
-    if (need > static_cast<int64_t>(a->free_q.size())) return PA_ERR_OOM;
+    if (need > a->nfree) return PA_ERR_OOM;
     pa_allocator::Seq s;
     s.table.reserve(static_cast<size_t>(need));
-    for (int64_t k = 0; k < need; ++k) {
-        const int32_t b = a->free_q.front();
-        a->free_q.pop_front();
-        a->ref[b] = 1;
-        s.table.push_back(b);
-    }
+    for (int64_t k = 0; k < need; ++k) s.table.push_back(a->take());
     s.len = num_tokens;
     a->seqs.emplace(seq, std::move(s));
     return PA_OK;
+}
+
+pa_status pa_seq_add_prefix(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                            int32_t num_tokens, int32_t* num_cached_tokens) {
+    if (!a || num_tokens < 0 || (num_tokens > 0 && !tokens)) return PA_ERR_INVALID_ARG;
+    if (a->seqs.count(seq)) return PA_ERR_STATE;
+    const int32_t B = a->block_size;
+    const int32_t eligible = num_tokens > 0 ? (num_tokens - 1) / B : 0;  // never the last token's block
+    std::vector<int32_t> hit;
+    uint64_t h = 0;
+    for (int32_t i = 0; i < eligible; ++i) {
+        const uint64_t hi = chain_hash(h, tokens + static_cast<int64_t>(i) * B, B);
+        auto it = a->cached.find(hi);
+        if (it == a->cached.end()) break;
+        hit.push_back(it->second);
+        h = hi;
+    }
+    const int64_t total = (static_cast<int64_t>(num_tokens) + B - 1) / B;
+    const int64_t need = total - static_cast<int64_t>(hit.size());
+    int64_t idle = 0;
+    for (int32_t b : hit) idle += a->ref[b] == 0;
+    if (need > a->nfree - idle) return PA_ERR_OOM;
+    a->lookups += eligible;
+    a->hits += static_cast<int64_t>(hit.size());
+    pa_allocator::Seq s;
+    s.table.reserve(static_cast<size_t>(total));
+    for (int32_t b : hit) {
+        if (a->ref[b] == 0) a->unlink(b);
+        a->ref[b] += 1;
+        s.table.push_back(b);
+    }
+    for (int64_t k = 0; k < need; ++k) s.table.push_back(a->take());
+    s.len = num_tokens;
+    s.reg_done = static_cast<int32_t>(hit.size());
+    s.reg_hash = h;
+    a->seqs.emplace(seq, std::move(s));
+    if (num_cached_tokens) *num_cached_tokens = static_cast<int32_t>(hit.size()) * B;
+    return PA_OK;
+}
+
+pa_status pa_seq_register_blocks(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                                 int32_t num_tokens) {
+    if (!a || num_tokens < 0 || (num_tokens > 0 && !tokens)) return PA_ERR_INVALID_ARG;
+    auto it = a->seqs.find(seq);
+    if (it == a->seqs.end()) return PA_ERR_STATE;
+    pa_allocator::Seq& s = it->second;
+    if (num_tokens > s.len) return PA_ERR_INVALID_ARG;
+    const int32_t B = a->block_size;
+    for (int32_t i = s.reg_done; i < num_tokens / B; ++i) {
+        s.reg_hash = chain_hash(s.reg_hash, tokens + static_cast<int64_t>(i) * B, B);
+        const int32_t b = s.table[i];
+        if (!a->is_cached[b] && !a->cached.count(s.reg_hash)) {
+            a->cached.emplace(s.reg_hash, b);
+            a->key[b] = s.reg_hash;
+            a->is_cached[b] = 1;
+        }
+        s.reg_done = i + 1;
+    }
+    return PA_OK;
+}
+
+pa_status pa_alloc_prefix_stats(const pa_allocator* a, int64_t* lookups, int64_t* hits,
+                                int32_t* cached_blocks) {
+    if (!a) return PA_ERR_INVALID_ARG;
+    if (lookups) *lookups = a->lookups;
+    if (hits) *hits = a->hits;
+    if (cached_blocks) *cached_blocks = static_cast<int32_t>(a->cached.size());
+    return PA_OK;
+}
+
+int32_t pa_alloc_block_cached(const pa_allocator* a, int32_t block, uint64_t* key) {
+    if (!a || block < 0 || block >= a->num_blocks) return -1;
+    if (!a->is_cached[block]) return 0;
+    if (key) *key = a->key[block];
+    return 1;
 }
 
 pa_status pa_seq_append(pa_allocator* a, int64_t seq, int64_t* slot, int32_t* cow_src,
@@ -175,9 +310,7 @@ pa_status pa_seq_free(pa_allocator* a, int64_t seq) {
     if (!a) return PA_ERR_INVALID_ARG;
     auto it = a->seqs.find(seq);
     if (it == a->seqs.end()) return PA_ERR_STATE;
-    for (int32_t b : it->second.table) {
-        if (--a->ref[b] == 0) a->free_q.push_back(b);
-    }
+    for (int32_t b : it->second.table) a->release_block(b);
     a->seqs.erase(it);
     return PA_OK;
 }

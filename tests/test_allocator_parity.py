@@ -19,6 +19,7 @@ def _snapshot(a: BlockAllocator, seqs):
         "ref": [a.refcount(b) for b in range(a.num_blocks)],
         "tables": {s: a.block_table(s) for s in sorted(seqs)},
         "lengths": {s: a.length(s) for s in sorted(seqs)},
+        "cached": a.cached_blocks(),
     }
 
 
@@ -149,3 +150,98 @@ def test_bad_initial_order_rejected():
         BlockAllocator(4, 16, [0, 1, 1, 2])
     with pytest.raises(PagedKVError):
         BlockAllocator(0, 16)
+
+
+# Prefix caching: prompts from a three-token alphabet with a few shared openings,
+# so that reuse, duplicates and evictions all happen on small pools.
+OPENINGS = [[1, 2, 1, 2, 3, 3, 1, 2], [2, 2, 2, 2, 1, 1, 1, 1], []]
+
+prefix_ops = st.lists(
+    st.one_of(
+        st.tuples(st.just("add_prefix"), st.integers(0, 7), st.integers(0, 2),
+                  st.lists(st.integers(1, 3), max_size=30)),
+        st.tuples(st.just("add"), st.integers(0, 7), st.integers(0, 40)),
+        st.tuples(st.just("register"), st.integers(0, 7), st.integers(0, 80)),
+        st.tuples(st.just("append"), st.integers(0, 7), st.integers(1, 3)),
+        st.tuples(st.just("fork"), st.integers(0, 7), st.integers(0, 7)),
+        st.tuples(st.just("free"), st.integers(0, 7)),
+    ),
+    min_size=1, max_size=80)
+
+
+@settings(max_examples=300, deadline=None)
+@given(ops=prefix_ops, nblocks=st.integers(1, 24), bs=st.sampled_from([1, 2, 4]),
+       seed=st.integers(0, 1000))
+def test_cpp_prefix_cache_matches_model(ops, nblocks, bs, seed):
+    order = np.random.default_rng(seed).permutation(nblocks)
+    model = am.AllocatorModel(nblocks, bs, order)
+    lib = BlockAllocator(nblocks, bs, order)
+    toks = {}
+    for op in ops:
+        name, seq = op[0], op[1]
+        if name == "add_prefix":
+            t = OPENINGS[op[2]] + op[3]
+            r = []
+            for side in (model, lib):
+                try:
+                    r.append(("ok", side.add_prefix(seq, t)))
+                except am.OutOfBlocks:
+                    r.append(("err", N.PA_ERR_OOM))
+                except am.BadState:
+                    r.append(("err", N.PA_ERR_STATE))
+                except PagedKVError as e:
+                    r.append(("err", e.status))
+            assert r[0] == r[1], (op, r)
+            if r[0][0] == "ok":
+                toks[seq] = list(t)
+        elif name == "register":
+            if seq not in toks:
+                continue
+            t = toks[seq][:op[2]]
+            model.register(seq, t)
+            lib.register(seq, t)
+        elif name == "append":
+            mres, lres = _apply(model, lib, ("append", seq))
+            assert mres == lres, (op, mres, lres)
+            if mres[0] == "ok":
+                toks[seq].append(op[2])
+        else:
+            mres, lres = _apply(model, lib, op)
+            assert mres[0] == lres[0], (op, mres, lres)
+            if mres[0] == "err":
+                assert mres[1] == lres[1], (op, mres, lres)
+            elif name == "add":
+                assert mres[1] == lres[1]
+                toks[seq] = [0] * op[2]
+            elif name == "fork":
+                toks[op[2]] = list(toks[seq])
+            elif name == "free":
+                del toks[seq]
+        assert _snapshot(lib, model.tables) == model.snapshot()
+        lk, ht, nc = lib.prefix_stats()
+        assert (lk, ht, nc) == (model.lookups, model.hits, len(model.cached))
+    lib.close()
+
+
+def test_cpp_prefix_cache_hand_worked_run():
+    """The six-block run worked by hand in test_prefix_cache.py, on the library."""
+    a = BlockAllocator(6, 4)
+    A = list(range(1, 11))
+    assert a.add_prefix(0, A) == 0 and a.block_table(0) == [0, 1, 2]
+    a.register(0, A)
+    h0 = am.chain_hash(0, [1, 2, 3, 4])
+    assert a.cached_blocks() == {0: h0, 1: am.chain_hash(h0, [5, 6, 7, 8])}
+    assert a.add_prefix(1, list(range(1, 9)) + [99, 100]) == 8 and a.block_table(1) == [0, 1, 3]
+    a.free(0)
+    a.free(1)
+    assert a.free_list() == [4, 5, 2, 0, 1, 3]
+    assert a.add_prefix(2, [1, 2, 3, 4, 7, 7, 7, 7, 5]) == 4
+    assert a.block_table(2) == [0, 4, 5] and a.free_list() == [2, 1, 3]
+    a.add(3, 8)
+    assert a.block_table(3) == [2, 1] and a.cached_blocks() == {0: h0}
+    with pytest.raises(PagedKVError) as e:
+        a.add_prefix(4, list(range(1, 10)))
+    assert e.value.status == N.PA_ERR_OOM and a.free_list() == [3] and a.refcount(0) == 1
+    assert a.add_prefix(5, [1, 2, 3, 4]) == 0 and a.block_table(5) == [3]
+    assert a.prefix_stats() == (6, 3, 1)
+    a.close()
