@@ -180,12 +180,13 @@ class AllocatorModel:
         tokens = [int(t) for t in tokens]
         n, B = len(tokens), self.block_size
         eligible = (n - 1) // B if n > 0 else 0   # never the block of the last token
-        hits, h = [], 0
+        hits, h = [], 0          # h: chain key after the reused blocks
         for i in range(eligible):
-            h = chain_hash(h, tokens[i * B:(i + 1) * B])
-            if h not in self.cached:
+            hi = chain_hash(h, tokens[i * B:(i + 1) * B])
+            if hi not in self.cached:
                 break
-            hits.append(self.cached[h])
+            hits.append(self.cached[hi])
+            h = hi
         need = -(-n // B) - len(hits)
         idle = sum(1 for b in hits if self.ref[b] == 0)
         if need > len(self.free) - idle:
@@ -199,7 +200,7 @@ class AllocatorModel:
         blocks = hits + [self._take() for _ in range(need)]
         self.tables[seq] = blocks
         self.lengths[seq] = n
-        self.progress[seq] = (len(hits), h if hits else 0)
+        self.progress[seq] = (len(hits), h)
         return len(hits) * B
 
     def register(self, seq: int, tokens) -> None:

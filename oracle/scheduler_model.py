@@ -33,6 +33,17 @@ Readings where the pages are silent (the library's scheduler takes the same):
   to the head of the waiting queue with its prompt extended by the tokens it
   has generated so far (recompute).  The append is then retried.
 
+* With prefix caching on, an arrival carries its prompt's token IDs and
+  admission goes through ``add_prefix``: the cached opening is not prefilled
+  (prefill starts after it), and the first request that does not fit blocks the
+  queue as before.  Each prompt chunk's full blocks are registered when the
+  chunk is planned (its K/V are written in that step, before any later step can
+  reuse them); after the step's decode appends, every decoding request's newly
+  full blocks are registered, in admission order.  Generated tokens have IDs
+  given by the workload; a preempted request is admitted again with its prompt
+  plus the tokens it generated, so its own cached blocks can serve the
+  recompute.
+
 Pins: a hand-worked trace on a four-block pool (tests/test_scheduler.py) that
 exercises admission, chunking, release, head-of-line blocking, and preemption
 of another request and of the requester itself; conservation of blocks after
@@ -56,6 +67,7 @@ class Request:
     prompt_eff: int = 0      # tokens to prefill at the latest admission
     prefilled: int = 0       # of prompt_eff written so far
     ready: bool = False      # prompt fully written in an earlier step
+    tokens: list = field(default_factory=list)  # prompt + generated token IDs (prefix caching)
 
     def finished(self) -> bool:
         return self.generated >= self.out_len
@@ -70,11 +82,16 @@ class StepRecord:
     prefill: list = field(default_factory=list)      # (rid, start, count, slots)
     preempted: list = field(default_factory=list)
     decode: list = field(default_factory=list)       # (rid, position, slot, cow)
+    cached: list = field(default_factory=list)       # (rid, cached prompt tokens) per admission
 
 
 class SchedulerModel:
-    def __init__(self, num_blocks: int, block_size: int, chunk: int, initial_free_order=None):
+    def __init__(self, num_blocks: int, block_size: int, chunk: int, initial_free_order=None,
+                 gen_token=None):
+        """gen_token(rid, position) -> token ID turns prefix caching on; arrivals
+        then carry (prompt token IDs, out_len)."""
         self.alloc = AllocatorModel(num_blocks, block_size, initial_free_order)
+        self.gen_token = gen_token
         self.B = block_size
         self.chunk = chunk
         self.waiting: deque[Request] = deque()
@@ -91,8 +108,12 @@ class SchedulerModel:
                 self.running.remove(r)
                 rec.finished.append(r.rid)
         # 2a. new requests queue up behind the waiting ones
+        prefix = self.gen_token is not None
         for prompt, out_len in arrivals:
-            r = Request(self.next_rid, int(prompt), int(out_len))
+            if prefix:
+                r = Request(self.next_rid, len(prompt), int(out_len), tokens=[int(t) for t in prompt])
+            else:
+                r = Request(self.next_rid, int(prompt), int(out_len))
             r.prompt_eff = r.prompt
             self.next_rid += 1
             self.waiting.append(r)
@@ -100,10 +121,18 @@ class SchedulerModel:
         # 2b. admit first come, first served while the whole prompt fits
         while self.waiting:
             r = self.waiting[0]
-            if -(-r.prompt_eff // self.B) > self.alloc.num_free():
-                break
-            self.alloc.add(r.rid, r.prompt_eff)
-            r.prefilled = 0
+            if prefix:
+                try:
+                    cached = self.alloc.add_prefix(r.rid, r.tokens[:r.prompt_eff])
+                except OutOfBlocks:
+                    break
+                rec.cached.append((r.rid, cached))
+            else:
+                if -(-r.prompt_eff // self.B) > self.alloc.num_free():
+                    break
+                self.alloc.add(r.rid, r.prompt_eff)
+                cached = 0
+            r.prefilled = cached
             r.ready = False
             self.running.append(r)
             self.waiting.popleft()
@@ -116,6 +145,8 @@ class SchedulerModel:
                 rec.prefill.append((r.rid, r.prefilled, c,
                                     self.alloc.slots(r.rid, r.prefilled, c)))
                 r.prefilled += c
+                if prefix:
+                    self.alloc.register(r.rid, r.tokens[:r.prefilled])
         # 3b. every decoding request appends one token (preempting when out of blocks)
         for r in decoders:
             while r in self.running:
@@ -131,9 +162,17 @@ class SchedulerModel:
                     self.waiting.appendleft(victim)
                     rec.preempted.append(victim.rid)
                     continue
-                rec.decode.append((r.rid, self.alloc.length(r.rid) - 1, slot, cow))
+                pos = self.alloc.length(r.rid) - 1
+                rec.decode.append((r.rid, pos, slot, cow))
                 r.generated += 1
+                if prefix:
+                    r.tokens.append(self.gen_token(r.rid, pos))
                 break
+        if prefix:
+            running = {r.rid: r for r in self.running}
+            for rid, *_ in rec.decode:
+                if rid in running:
+                    self.alloc.register(rid, running[rid].tokens)
         # a prompt written this step decodes from the next one
         for r in self.running:
             if not r.ready and r.prefilled == r.prompt_eff:

@@ -16,8 +16,14 @@ Batching原理与实践", section 2.3):
    are released and it rejoins the head of the queue to recompute its prompt
    plus the tokens it has generated (hihuo.com page, Preemption（抢占）).
 
+With prefix caching (``gen_token`` given), arrivals carry their prompts' token
+IDs; admission reuses the cached opening of each prompt through the allocator's
+``add_prefix`` (hihuo.com page, 优势 > 3. 支持共享), prefill starts after it, each
+planned chunk's full blocks are registered, and after the decode appends every
+decoding request's newly full blocks are registered, in admission order.
+
 The plan a step returns says which slots to write and which sequences to decode;
-the caller performs the device work (cache writes, then decode attention).
+the caller performs the device work (cache writes, then attention).
 """
 
 from __future__ import annotations
@@ -41,6 +47,7 @@ class _Req:
     prefilled: int = 0
     ready: bool = False
     length: int = 0   # tokens held in the cache
+    tokens: list = field(default_factory=list)  # prompt + generated token IDs (prefix caching)
 
 
 @dataclass
@@ -55,14 +62,19 @@ class StepPlan:
     decode_pos: np.ndarray = None                 # int64[n]: position of the new token
     decode_slots: np.ndarray = None               # int64[n]
     decode_cows: np.ndarray = None                # int32[n, 2], -1 = no copy
+    cached: list = field(default_factory=list)    # (rid, cached prompt tokens) per admission
 
     def prefill_tokens(self) -> int:
         return sum(c for _, _, c, _ in self.prefill)
 
 
 class TraceScheduler:
-    def __init__(self, num_blocks: int, block_size: int, chunk: int, initial_free_order=None):
+    def __init__(self, num_blocks: int, block_size: int, chunk: int, initial_free_order=None,
+                 gen_token=None):
+        """gen_token(rid, position) -> token ID turns prefix caching on; arrivals
+        then carry (prompt token IDs, out_len)."""
         self.alloc = BlockAllocator(num_blocks, block_size, initial_free_order)
+        self.gen_token = gen_token
         self.B = block_size
         self.chunk = chunk
         self.waiting: deque[_Req] = deque()
@@ -81,19 +93,34 @@ class TraceScheduler:
             else:
                 keep.append(r)
         self.running = keep
+        prefix = self.gen_token is not None
         for prompt, out_len in arrivals:
-            r = _Req(self.next_rid, int(prompt), int(out_len))
+            if prefix:
+                r = _Req(self.next_rid, len(prompt), int(out_len),
+                         tokens=np.asarray(prompt, dtype=np.int32).tolist())
+            else:
+                r = _Req(self.next_rid, int(prompt), int(out_len))
             r.prompt_eff = r.prompt
             self.next_rid += 1
             self.waiting.append(r)
             plan.arrived.append(r.rid)
         while self.waiting:
             r = self.waiting[0]
-            if -(-r.prompt_eff // self.B) > alloc.num_free():
-                break
-            alloc.add(r.rid, r.prompt_eff)
+            if prefix:
+                try:
+                    cached = alloc.add_prefix(r.rid, r.tokens[:r.prompt_eff])
+                except N.PagedKVError as e:
+                    if e.status != N.PA_ERR_OOM:
+                        raise
+                    break
+                plan.cached.append((r.rid, cached))
+            else:
+                if -(-r.prompt_eff // self.B) > alloc.num_free():
+                    break
+                alloc.add(r.rid, r.prompt_eff)
+                cached = 0
             r.length = r.prompt_eff
-            r.prefilled = 0
+            r.prefilled = cached
             r.ready = False
             self.running.append(r)
             self.waiting.popleft()
@@ -104,6 +131,8 @@ class TraceScheduler:
                 c = min(self.chunk, r.prompt_eff - r.prefilled)
                 plan.prefill.append((r.rid, r.prefilled, c, alloc.slots(r.rid, r.prefilled, c)))
                 r.prefilled += c
+                if prefix:
+                    alloc.register(r.rid, r.tokens[:r.prefilled])
         rids, slots, cows, pos = [], [], [], []
         pending = decoders
         while pending:
@@ -114,6 +143,8 @@ class TraceScheduler:
                 slots.append(sl[k])
                 cows.append(cw[k])
                 pos.append(pending[k].length)
+                if prefix:
+                    pending[k].tokens.append(self.gen_token(pending[k].rid, pending[k].length))
                 pending[k].length += 1
                 pending[k].generated += 1
             if st == N.PA_OK:
@@ -129,6 +160,11 @@ class TraceScheduler:
             self.waiting.appendleft(victim)
             plan.preempted.append(victim.rid)
             pending = [r for r in pending[done:] if r is not victim]
+        if prefix:
+            running = {r.rid: r for r in self.running}
+            for rid in rids:
+                if rid in running:
+                    alloc.register(rid, running[rid].tokens)
         for r in self.running:
             if not r.ready and r.prefilled == r.prompt_eff:
                 r.ready = True

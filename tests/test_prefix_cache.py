@@ -129,3 +129,15 @@ def _content_safety_run(seed, steps=400):
 def test_content_safety_random_runs(seed):
     m = _content_safety_run(seed)
     assert m.hits > 0                                  # the runs did exercise reuse
+
+
+def test_progress_after_a_partial_hit_continues_the_chain():
+    """A prompt whose first block hits and second misses registers its second block
+    under the key chained from the first (the reused one), not from the miss."""
+    m = AllocatorModel(8, 2)
+    m.add_prefix(0, [1, 2, 3])
+    m.register(0, [1, 2, 3])
+    assert m.add_prefix(1, [1, 2, 5, 6, 7]) == 2
+    m.register(1, [1, 2, 5, 6, 7])
+    h0 = chain_hash(0, [1, 2])
+    assert m.snapshot()["cached"][m.block_table(1)[1]] == chain_hash(h0, [5, 6])

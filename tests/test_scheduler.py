@@ -112,3 +112,38 @@ def test_library_scheduler_equals_model_on_trace(num_blocks, steps):
     assert [r.rid for r in model.waiting] == lib.waiting_ids()
     if num_blocks is not None and num_blocks <= 20000:
         assert preempted > 0, "the small pool was meant to force preemption"
+
+
+def _plan_cached(plan):
+    return [(int(r), int(c)) for r, c in plan.cached]
+
+
+@pytest.mark.parametrize("name,num_blocks,steps", [("trace_prefix_small", None, 48),
+                                                   ("trace_prefix_small", 120, 48),
+                                                   ("trace_prefix", None, 120),
+                                                   ("trace_prefix", 6000, 120)])
+def test_library_scheduler_equals_model_with_prefix_caching(name, num_blocks, steps):
+    """Prompts opening with shared system prompts: admissions reuse cached blocks,
+    prefill starts after the cached opening; at the config's pool and at pools small
+    enough to preempt (a preempted request recomputes from its own cached blocks)."""
+    cfg = CONFIGS[name]
+    N = num_blocks or cfg.num_blocks
+    order = gen.pool_permutation(cfg.seed, N)
+    model = SchedulerModel(N, cfg.block_size, cfg.chunk, order, gen_token=cfg.gen_token)
+    lib = TraceScheduler(N, cfg.block_size, cfg.chunk, order, gen_token=cfg.gen_token)
+    preempted = cached = 0
+    for n in range(steps):
+        arr = cfg.arrivals(n)
+        rec = model.step(n, arr)
+        plan = lib.step(n, arr)
+        assert _plan_events(plan) == _model_events(rec), f"step {n}"
+        assert _plan_cached(plan) == rec.cached, f"step {n}"
+        preempted += len(rec.preempted)
+        cached += sum(c for _, c in rec.cached)
+        if n % 10 == 0 or n == steps - 1:
+            assert lib.alloc.free_list() == model.alloc.free_list()
+            assert lib.alloc.cached_blocks() == model.alloc.snapshot()["cached"]
+    assert cached > 0, "the shared openings were meant to be reused"
+    assert lib.alloc.prefix_stats() == (model.alloc.lookups, model.alloc.hits, len(model.alloc.cached))
+    if num_blocks is not None:
+        assert preempted > 0, "the small pool was meant to force preemption"

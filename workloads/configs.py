@@ -91,6 +91,14 @@ class TraceConfig:
     out_lo: int
     out_hi: int
     chunk: int
+    # prefix caching: prompts open with one of `openings` shared system prompts
+    # (0 = plain prompts of the lengths above, no token IDs)
+    openings: int = 0
+    open_lo: int = 0
+    open_hi: int = 0
+    suffix_lo: int = 0
+    suffix_hi: int = 0
+    vocab: int = 64
 
     @property
     def scale(self) -> float:
@@ -99,6 +107,24 @@ class TraceConfig:
     @property
     def group(self) -> int:
         return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def prefix(self) -> bool:
+        return self.openings > 0
+
+    def arrivals(self, step: int):
+        """Requests arriving at `step`: (prompt length, out_len) pairs, or with shared
+        openings (prompt token IDs, out_len) pairs."""
+        p, o = gen.trace_arrivals(self.seed, step, self.arrival_mean, self.prompt_lo,
+                                  self.prompt_hi, self.out_p, self.out_lo, self.out_hi)
+        if not self.prefix:
+            return list(zip(p.tolist(), o.tolist()))
+        toks = gen.shared_opening_prompts(self.seed, step, len(p), self.openings, self.open_lo,
+                                          self.open_hi, self.suffix_lo, self.suffix_hi, self.vocab)
+        return list(zip(toks, o.tolist()))
+
+    def gen_token(self, rid: int, position: int) -> int:
+        return gen.generated_token(self.seed, rid, position, self.vocab)
 
 
 @dataclass(frozen=True)
@@ -170,6 +196,20 @@ CONFIGS = {
         name="prefill_gqa", title="chunked prefill, 8 chunks of 512 after U[0,3584] cached tokens, "
         "32q/8kv x 128, bf16", seed=8, dtype="bf16", num_seqs=8, num_q_heads=32, num_kv_heads=8,
         head_dim=128, block_size=16, num_blocks=4096, chunk=512, offset_lo=0, offset_hi=3584),
+    # serving trace whose prompts open with one of 8 shared system prompts
+    "trace_prefix": TraceConfig(
+        name="trace_prefix", title="continuous-batching trace with prefix caching: 8 shared "
+        "system prompts of 256-1024 tokens + private suffixes of 16-256, 40x128 heads, bf16",
+        seed=9, dtype="bf16", num_q_heads=40, num_kv_heads=40, head_dim=128, block_size=16,
+        num_blocks=50000, steps=200, arrival_mean=8.0, prompt_lo=0, prompt_hi=0,
+        out_p=0.01, out_lo=10, out_hi=500, chunk=512, openings=8, open_lo=256, open_hi=1024,
+        suffix_lo=16, suffix_hi=256, vocab=64),
+    "trace_prefix_small": TraceConfig(
+        name="trace_prefix_small", title="prefix-caching trace, 48 steps, small pool, bf16",
+        seed=17, dtype="bf16", num_q_heads=8, num_kv_heads=4, head_dim=128, block_size=16,
+        num_blocks=200, steps=48, arrival_mean=2.0, prompt_lo=0, prompt_hi=0,
+        out_p=0.08, out_lo=2, out_hi=40, chunk=64, openings=3, open_lo=20, open_hi=120,
+        suffix_lo=4, suffix_hi=60, vocab=64),
     # small trace for GPU parity tests: same loop, a pool small enough to preempt
     "trace_small": TraceConfig(
         name="trace_small", title="continuous-batching trace, 48 steps, small pool, bf16",

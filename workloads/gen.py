@@ -9,6 +9,8 @@ returned as raw ``uint16`` bit patterns, float32 data is returned as float32.
 
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 
 # Sub-stream tags: the second word of every seed sequence.
@@ -124,3 +126,56 @@ def trace_query(seed: int, req: int, position: int, num_q_heads: int, head_dim: 
                 dtype: str) -> np.ndarray:
     """Query [Hq, D] of request `req` at the decode step that writes `position`."""
     return draw_values(stream(seed, TAG_TRACE_Q, req, position), (num_q_heads, head_dim), dtype)
+
+
+# ----------------------------------------------------------------------------- shared prompt openings
+
+TAG_TOKEN_KV = 9    # per-token and per-position tables of content-addressed keys/values
+TAG_PROMPTS = 10    # token IDs of the prompts of a serving trace with shared openings
+TAG_GEN_TOKEN = 11  # token IDs a request generates
+
+
+@functools.lru_cache(maxsize=4)
+def _token_kv_tables(seed: int, num_kv_heads: int, head_dim: int, vocab: int, max_pos: int):
+    shape = (2, num_kv_heads, head_dim)
+    tok_t = stream(seed, TAG_TOKEN_KV, 0).standard_normal((vocab, *shape), dtype=np.float32)
+    pos_t = stream(seed, TAG_TOKEN_KV, 1).standard_normal((max_pos, *shape), dtype=np.float32)
+    return tok_t, pos_t
+
+
+def token_kv(seed: int, tokens, start: int, num_kv_heads: int, head_dim: int, dtype: str,
+             vocab: int = 64, max_pos: int = 8192):
+    """Keys and values of `tokens` at positions start, start+1, ...: two [n, Hkv, D].
+
+    A token's values depend only on (seed, token ID, position) - a per-token draw
+    plus a per-position draw, summed in float32 and rounded once - so prompts that
+    share an opening hold identical bits there, as a model's cache would."""
+    tokens = np.asarray(tokens, dtype=np.int64).reshape(-1)
+    pos = start + np.arange(len(tokens))
+    if len(tokens) and (tokens.min() < 0 or tokens.max() >= vocab or pos[-1] >= max_pos):
+        raise ValueError("token or position outside the tables")
+    tok_t, pos_t = _token_kv_tables(seed, num_kv_heads, head_dim, vocab, max_pos)
+    x = (tok_t[tokens] + pos_t[pos]) * np.float32(0.7071067811865476)
+    x = x if dtype == "f32" else bf16_bits_from_f32(x)
+    return x[:, 0], x[:, 1]
+
+
+def shared_opening_prompts(seed: int, step: int, count: int, openings: int, open_lo: int,
+                           open_hi: int, suffix_lo: int, suffix_hi: int, vocab: int):
+    """Token IDs of `count` prompts arriving at one step: each is one of `openings`
+    fixed openings (a system prompt, its length uniform on [open_lo, open_hi] and
+    drawn once per trace) followed by a private suffix of uniform length."""
+    lens = stream(seed, TAG_PROMPTS, 0).integers(open_lo, open_hi + 1, openings)
+    heads = [stream(seed, TAG_PROMPTS, 1, k).integers(0, vocab, int(lens[k])) for k in range(openings)]
+    rng = stream(seed, TAG_PROMPTS, 2, step)
+    out = []
+    for _ in range(count):
+        k = int(rng.integers(0, openings))
+        tail = rng.integers(0, vocab, int(rng.integers(suffix_lo, suffix_hi + 1)))
+        out.append(np.concatenate([heads[k], tail]).astype(np.int32))
+    return out
+
+
+def generated_token(seed: int, req: int, position: int, vocab: int) -> int:
+    """Token ID request `req` produces at `position`."""
+    return int(stream(seed, TAG_GEN_TOKEN, req, position).integers(0, vocab))
