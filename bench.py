@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gqa_b256",
                     choices=["gqa_b256", "llama2_7b_b64", "shared_prefix_b16", "shared_prefix_b32",
-                             "trace_13b", "prefill_13b", "prefill_gqa"])
+                             "trace_13b", "trace_prefix", "prefill_13b", "prefill_gqa"])
     ap.add_argument("--units", type=int, default=0, help="decode work units (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -156,8 +156,10 @@ def cpu_baseline(cfg, ctx, q_host, seconds):
 def run_trace(args):
     """The continuous-batching trace: the library scheduler plans every step on the
     host (timed separately), then each step's device work runs on inputs already in
-    HBM - the prompt chunks' cache writes, the decode tokens' writes, and decode
-    attention over every decoding sequence - timed with events around each step."""
+    HBM - the prompt chunks' cache writes, chunked-prefill attention over them, the
+    decode tokens' writes, and decode attention over every decoding sequence - timed
+    with events around each step.  With shared prompt openings (prefix caching) the
+    cached part of a prompt is neither written nor attended again."""
     import torch
     from paged_kv_cache_397_amd import ops, _native
     from paged_kv_cache_397_amd.scheduler import TraceScheduler
@@ -168,17 +170,32 @@ def run_trace(args):
     B, D, Hq, Hkv = cfg.block_size, cfg.head_dim, cfg.num_q_heads, cfg.num_kv_heads
     spec = ops.CacheSpec(cfg.num_blocks, B, Hkv, D, cfg.dtype)
     max_blocks = -(-(cfg.prompt_hi + cfg.out_hi) // B)
-    sched = TraceScheduler(cfg.num_blocks, B, cfg.chunk, gen.pool_permutation(cfg.seed, cfg.num_blocks))
+    if cfg.prefix:
+        max_blocks = -(-(cfg.open_hi + cfg.suffix_hi + cfg.out_hi) // B)
+    order = gen.pool_permutation(cfg.seed, cfg.num_blocks)
+    sched = TraceScheduler(cfg.num_blocks, B, cfg.chunk, order,
+                           gen_token=cfg.gen_token if cfg.prefix else None)
+    arrivals = [cfg.arrivals(n) for n in range(cfg.steps)]
     plans, host_s = [], []
     for n in range(cfg.steps):
-        p, o = gen.trace_arrivals(cfg.seed, n, cfg.arrival_mean, cfg.prompt_lo, cfg.prompt_hi,
-                                  cfg.out_p, cfg.out_lo, cfg.out_hi)
         t0 = time.perf_counter()
-        plan = sched.step(n, list(zip(p.tolist(), o.tolist())))
+        plan = sched.step(n, arrivals[n])
         tables, ctx = sched.alloc.batch_metadata(plan.decode_rids, max_blocks)
+        prids = np.array([r for r, _, _, _ in plan.prefill], dtype=np.int64)
+        ptables, _ = sched.alloc.batch_metadata(prids, max_blocks)
         host_s.append(time.perf_counter() - t0)
-        plans.append((plan, tables, ctx))
+        plans.append((plan, tables, ctx, ptables))
     log(f"scheduled {cfg.steps} steps on the host")
+    # the oracle scheduling model over the same trace, timed the same way (host side)
+    from oracle.scheduler_model import SchedulerModel
+    model = SchedulerModel(cfg.num_blocks, B, cfg.chunk, order,
+                           gen_token=cfg.gen_token if cfg.prefix else None)
+    model_s = []
+    model_steps = min(cfg.steps, 40)  # a bounded sample: the model is plain Python
+    for n in range(model_steps):
+        t0 = time.perf_counter()
+        model.step(n, arrivals[n])
+        model_s.append(time.perf_counter() - t0)
     # Inputs resident in HBM: per-step metadata, and seeded synthetic K/V/q drawn on
     # the device (values do not affect timing; the parity of this loop is a test).
     g = torch.Generator(device="cuda")
@@ -187,14 +204,25 @@ def run_trace(args):
     kc.zero_()
     vc.zero_()
     steps_dev = []
-    for plan, tables, ctx in plans:
+    for plan, tables, ctx, ptables in plans:
         P = plan.prefill_tokens()
         S = len(plan.decode_rids)
-        d = {"P": P, "S": S, "ctx_sum": int(ctx.sum())}
+        d = {"P": P, "S": S, "ctx_sum": int(ctx.sum()),
+             "cached": int(sum(c for _, c in plan.cached))}
         if P:
             d["pslots"] = torch.from_numpy(np.concatenate([sl for _, _, _, sl in plan.prefill])).cuda()
             d["pk"] = torch.randn(P, Hkv, D, generator=g, device="cuda", dtype=spec.torch_dtype)
             d["pv"] = torch.randn(P, Hkv, D, generator=g, device="cuda", dtype=spec.torch_dtype)
+            cl = np.array([c for _, _, c, _ in plan.prefill], dtype=np.int64)
+            st = np.array([s0 for _, s0, _, _ in plan.prefill], dtype=np.int64)
+            d["pq"] = torch.randn(P, Hq, D, generator=g, device="cuda", dtype=spec.torch_dtype)
+            d["pout"] = torch.empty(P, Hq, D, device="cuda", dtype=spec.torch_dtype)
+            d["pqs"] = torch.from_numpy(np.concatenate([[0], np.cumsum(cl)]).astype(np.int32)).cuda()
+            d["pctx"] = torch.from_numpy((st + cl).astype(np.int32)).cuda()
+            d["ptables"] = torch.from_numpy(ptables).cuda()
+            d["pmax"] = int(cl.max())
+            d["pflops"] = float(sum(4.0 * D * Hq * (c * s0 + c * (c + 1) // 2)
+                                    for s0, c in zip(st.tolist(), cl.tolist())))
         if S:
             d["dslots"] = torch.from_numpy(plan.decode_slots).cuda()
             d["cows"] = torch.from_numpy(np.ascontiguousarray(plan.decode_cows)).cuda()
@@ -212,11 +240,17 @@ def run_trace(args):
     stream = torch.cuda.current_stream()
     evs = []
     t0 = time.perf_counter()
+    evp = []
     for d in steps_dev:
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0, e1, e2, ep0, ep1 = (torch.cuda.Event(enable_timing=True) for _ in range(5))
         e0.record(stream)
+        ep0.record(stream)
         if d["P"]:
             ops.reshape_and_cache(spec, d["pk"], d["pv"], d["pslots"], kc, vc)
+            ops.paged_attn_prefill(spec, d["pout"], d["pq"], kc, vc, d["ptables"], d["pqs"],
+                                   d["pctx"], cfg.scale, max_query_len=d["pmax"])
+        ep1.record(stream)
+        evp.append((ep0, ep1))
         if d["S"]:
             ops.append_tokens(spec, d["k"], d["v"], d["dslots"], kc, vc, cow_pairs=d["cows"])
             e1.record(stream)
@@ -230,6 +264,8 @@ def run_trace(args):
     wall = time.perf_counter() - t0
     t_step = np.array([a.elapsed_time(c) for a, _, c in evs]) * 1e-3
     t_attn = np.array([b.elapsed_time(c) for _, b, c in evs]) * 1e-3
+    t_pre = np.array([a.elapsed_time(b) for a, b in evp]) * 1e-3
+    pflops = np.array([d.get("pflops", 0.0) for d in steps_dev])
     kv_tok = 2 * Hkv * D * spec_elem_bytes(cfg.dtype)
     kv_bytes = np.array([d["ctx_sum"] for d in steps_dev], dtype=np.float64) * kv_tok
     lo = min(50, cfg.steps - 1)
@@ -260,8 +296,18 @@ def run_trace(args):
         "decode_seqs_last_step": steps_dev[-1]["S"],
         "decode_kv_gb_last_step": round(float(kv_bytes[-1]) / 1e9, 3),
         "prefill_tokens_per_step_mean": round(float(np.mean([d["P"] for d in steps_dev[lo:]])), 1),
+        "prefill_us_per_step_mean": round(float(t_pre[sel].mean()) * 1e6, 2),
+        "prefill_attn_tflops": round(float(pflops[sel].sum() / max(t_pre[sel].sum(), 1e-12) / 1e12), 2),
+        "prefix_cache": ({"cached_prompt_tokens_per_step_mean":
+                          round(float(np.mean([d["cached"] for d in steps_dev[lo:]])), 1),
+                          "blocks_looked_up_reused_cached_now": list(sched.alloc.prefix_stats())}
+                         if cfg.prefix else None),
         "host_scheduler_us_per_step": {"mean": round(float(np.mean(host_s[lo:])) * 1e6, 2),
                                        "p99": round(float(np.percentile(host_s[lo:], 99)) * 1e6, 2)},
+        "oracle_scheduler": {"kind": "oracle", "steps": f"0..{model_steps - 1}",
+                             "us_per_step_mean": round(float(np.mean(model_s)) * 1e6, 2),
+                             "library_us_per_step_mean_same_steps":
+                                 round(float(np.mean(host_s[:model_steps])) * 1e6, 2)},
         "wall_ms_all_steps": round(wall * 1e3, 2),
     }
     print(json.dumps(result), flush=True)
@@ -414,7 +460,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
-    if args.config == "trace_13b":
+    if args.config.startswith("trace"):
         run_trace(args)
         return
     if args.config.startswith("prefill"):

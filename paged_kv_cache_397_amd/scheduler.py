@@ -47,7 +47,14 @@ class _Req:
     prefilled: int = 0
     ready: bool = False
     length: int = 0   # tokens held in the cache
-    tokens: list = field(default_factory=list)  # prompt + generated token IDs (prefix caching)
+    tokens: np.ndarray = None  # prompt + generated token IDs (prefix caching), int32, with room
+    ntok: int = 0
+
+    def push(self, t: int):
+        if self.ntok == len(self.tokens):
+            self.tokens = np.concatenate([self.tokens, np.empty_like(self.tokens)])
+        self.tokens[self.ntok] = t
+        self.ntok += 1
 
 
 @dataclass
@@ -96,8 +103,11 @@ class TraceScheduler:
         prefix = self.gen_token is not None
         for prompt, out_len in arrivals:
             if prefix:
-                r = _Req(self.next_rid, len(prompt), int(out_len),
-                         tokens=np.asarray(prompt, dtype=np.int32).tolist())
+                p = np.asarray(prompt, dtype=np.int32)
+                r = _Req(self.next_rid, len(p), int(out_len))
+                r.tokens = np.empty(len(p) + int(out_len) + 1, dtype=np.int32)
+                r.tokens[:len(p)] = p
+                r.ntok = len(p)
             else:
                 r = _Req(self.next_rid, int(prompt), int(out_len))
             r.prompt_eff = r.prompt
@@ -144,7 +154,7 @@ class TraceScheduler:
                 cows.append(cw[k])
                 pos.append(pending[k].length)
                 if prefix:
-                    pending[k].tokens.append(self.gen_token(pending[k].rid, pending[k].length))
+                    pending[k].push(self.gen_token(pending[k].rid, pending[k].length))
                 pending[k].length += 1
                 pending[k].generated += 1
             if st == N.PA_OK:
@@ -161,10 +171,13 @@ class TraceScheduler:
             plan.preempted.append(victim.rid)
             pending = [r for r in pending[done:] if r is not victim]
         if prefix:
+            # only a token that completes a block can add one to the cache; the
+            # other calls would change nothing
             running = {r.rid: r for r in self.running}
-            for rid in rids:
-                if rid in running:
-                    alloc.register(rid, running[rid].tokens)
+            for rid, p in zip(rids, pos):
+                if (p + 1) % self.B == 0 and rid in running:
+                    rr = running[rid]
+                    alloc.register(rid, rr.tokens[:rr.ntok])
         for r in self.running:
             if not r.ready and r.prefilled == r.prompt_eff:
                 r.ready = True

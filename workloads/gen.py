@@ -176,6 +176,19 @@ def shared_opening_prompts(seed: int, step: int, count: int, openings: int, open
     return out
 
 
+_M64 = (1 << 64) - 1
+
+
+def _splitmix64(x: int) -> int:
+    """One output of the SplitMix64 generator (Steele, Lea and Flood) for state x."""
+    z = (x + 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
 def generated_token(seed: int, req: int, position: int, vocab: int) -> int:
-    """Token ID request `req` produces at `position`."""
-    return int(stream(seed, TAG_GEN_TOKEN, req, position).integers(0, vocab))
+    """Token ID request `req` produces at `position` (a counter-based draw: cheap
+    enough to call once per generated token)."""
+    x = _splitmix64((int(seed) << 48) ^ (TAG_GEN_TOKEN << 40) ^ (int(req) << 20) ^ int(position))
+    return int(x % vocab)
