@@ -61,6 +61,17 @@ again (hihuo.com page, 优势 > 3. 支持共享; ksqn.cn page, 3.4 and 5.2 item 
   an allocation takes it from the head of the queue.  The FIFO queue is thereby
   least-recently-freed-first.
 
+Swapping.  A suspended request's pages can be moved to CPU memory and brought
+back later instead of being recomputed (hihuo.com page, Preemption（抢占）: the
+two modes Recompute and Swap; ksqn.cn page, 3.4 on ``--swap-space``).  Readings:
+a host pool of fixed-size blocks with its own FIFO free queue; ``swap_out`` is
+all-or-nothing, gives the sequence one host block per table entry (in logical
+order, taken from the host queue's head), and drops its device references as
+``release`` would (a shared block stays for its other holders); ``swap_in``
+takes fresh device blocks from the queue's head and returns the host blocks to
+the host queue's tail in logical order.  A swapped sequence keeps its length and
+prefix-cache progress; anything but ``swap_in`` or ``release`` on it is BadState.
+
 Prefix-cache pins: published FNV-1a-64 test vectors; a hand-worked run on a
 six-block pool (tests/test_prefix_cache.py); content safety over random runs
 (every reused block holds exactly the tokens the new prompt has at that place).
@@ -108,7 +119,8 @@ class BadArgument(AllocError):
 
 
 class AllocatorModel:
-    def __init__(self, num_blocks: int, block_size: int, initial_free_order=None):
+    def __init__(self, num_blocks: int, block_size: int, initial_free_order=None,
+                 num_host_blocks: int = 0):
         if num_blocks <= 0 or block_size <= 0:
             raise BadArgument("num_blocks and block_size must be positive")
         order = list(range(num_blocks)) if initial_free_order is None else [int(b) for b in initial_free_order]
@@ -127,6 +139,8 @@ class AllocatorModel:
         self.progress: dict[int, tuple[int, int]] = {}
         self.lookups = 0
         self.hits = 0
+        self.host_free = deque(range(num_host_blocks))
+        self.swapped: dict[int, list[int]] = {}   # sequence -> host blocks, logical order
 
     # -- queries ---------------------------------------------------------------
     def num_free(self) -> int:
@@ -158,7 +172,7 @@ class AllocatorModel:
     # -- operations ------------------------------------------------------------
     def add(self, seq: int, num_tokens: int) -> list[int]:
         """Admit a new sequence holding ``num_tokens`` tokens."""
-        if seq in self.tables:
+        if seq in self.tables or seq in self.swapped:
             raise BadState(f"sequence {seq} already exists")
         if num_tokens < 0:
             raise BadArgument("negative token count")
@@ -175,7 +189,7 @@ class AllocatorModel:
         """Admit a new sequence whose prompt is ``tokens``, reusing cached blocks
         for the longest cached run of its leading full blocks.  Returns the number
         of prompt tokens whose K/V are already in the cache."""
-        if seq in self.tables:
+        if seq in self.tables or seq in self.swapped:
             raise BadState(f"sequence {seq} already exists")
         tokens = [int(t) for t in tokens]
         n, B = len(tokens), self.block_size
@@ -261,7 +275,7 @@ class AllocatorModel:
     def fork(self, parent: int, child: int) -> None:
         """New sequence ``child`` sharing every block of ``parent``."""
         self._need(parent)
-        if child in self.tables:
+        if child in self.tables or child in self.swapped:
             raise BadState(f"sequence {child} already exists")
         t = list(self.tables[parent])
         for b in t:
@@ -270,8 +284,43 @@ class AllocatorModel:
         self.lengths[child] = self.lengths[parent]
         self.progress[child] = self.progress[parent]
 
+    def swap_out(self, seq: int) -> list[tuple[int, int]]:
+        """Move the sequence to host blocks; returns (device block, host block) pairs
+        to copy, in logical order."""
+        self._need(seq)
+        table = self.tables[seq]
+        if len(table) > len(self.host_free):
+            raise OutOfBlocks(f"need {len(table)} host blocks, {len(self.host_free)} free")
+        pairs = [(b, self.host_free.popleft()) for b in table]
+        for b in table:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        self.swapped[seq] = [h for _, h in pairs]
+        del self.tables[seq]
+        return pairs
+
+    def swap_in(self, seq: int) -> list[tuple[int, int]]:
+        """Bring a swapped sequence back to fresh device blocks; returns (host block,
+        device block) pairs to copy, in logical order."""
+        if seq not in self.swapped:
+            raise BadState(f"sequence {seq} is not swapped out")
+        host = self.swapped[seq]
+        if len(host) > len(self.free):
+            raise OutOfBlocks(f"need {len(host)} blocks, {len(self.free)} free")
+        blocks = [self._take() for _ in host]
+        self.host_free.extend(host)
+        self.tables[seq] = blocks
+        del self.swapped[seq]
+        return list(zip(host, blocks))
+
     def release(self, seq: int) -> None:
         """Drop the sequence; blocks whose count reaches zero join the free tail."""
+        if seq in self.swapped:
+            self.host_free.extend(self.swapped.pop(seq))
+            del self.lengths[seq]
+            del self.progress[seq]
+            return
         self._need(seq)
         for b in self.tables[seq]:
             self.ref[b] -= 1
@@ -294,4 +343,6 @@ class AllocatorModel:
             "tables": {s: list(t) for s, t in sorted(self.tables.items())},
             "lengths": dict(sorted(self.lengths.items())),
             "cached": dict(sorted(self.block_hash.items())),
+            "host_free": list(self.host_free),
+            "swapped": {s: list(t) for s, t in sorted(self.swapped.items())},
         }

@@ -14,8 +14,14 @@
   reading).  ``copy_blocks`` copies every byte of the K and V data of ``src``
   onto ``dst``, pair by pair in the order given.
 
+* Preemption by swapping moves a suspended request's K/V blocks to CPU memory
+  and back (hihuo.com page, Preemption（抢占）: Swap; ksqn.cn page, 3.4 on
+  ``--swap-space``).  ``swap_blocks`` copies whole blocks from one pool to another
+  pool of the same block geometry (device to host, or back), pair by pair.
+
 Pins: write-then-gather returns the written tokens; bytes of untouched slots are
-unchanged; slot -1 writes nothing; a copied block reads back equal to its source.
+unchanged; slot -1 writes nothing; a copied block reads back equal to its source;
+a sequence swapped out and in through different blocks gathers back unchanged.
 """
 
 from __future__ import annotations
@@ -43,3 +49,18 @@ def copy_blocks(layout: CacheLayout, k_cache, v_cache, pairs) -> None:
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():
         kb[dst] = kb[src]
         vb[dst] = vb[src]
+
+
+def swap_blocks(src_layout: CacheLayout, src_k, src_v, dst_layout: CacheLayout, dst_k, dst_v,
+                pairs) -> None:
+    """For each (src, dst) pair, copy block src of one pool onto block dst of another
+    pool with the same block geometry."""
+    n = src_layout.block_elems()
+    assert dst_layout.block_elems() == n
+    sk = src_k.reshape(src_layout.num_blocks, n)
+    sv = src_v.reshape(src_layout.num_blocks, n)
+    dk = dst_k.reshape(dst_layout.num_blocks, n)
+    dv = dst_v.reshape(dst_layout.num_blocks, n)
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():
+        dk[dst] = sk[src]
+        dv[dst] = sv[src]
