@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gqa_b256",
                     choices=["gqa_b256", "llama2_7b_b64", "shared_prefix_b16", "shared_prefix_b32",
-                             "trace_13b", "trace_prefix", "prefill_13b", "prefill_gqa"])
+                             "trace_13b", "trace_prefix", "prefill_13b", "prefill_gqa", "swap_13b"])
     ap.add_argument("--units", type=int, default=0, help="decode work units (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -450,6 +450,99 @@ def run_prefill(args):
     print(json.dumps(result), flush=True)
 
 
+PCIE_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction, raw
+
+
+def run_swap(args):
+    """Swap preemption's data path: blocks of a 13B-shaped layer (40 KV heads x 16
+    tokens x 128 dims, bf16: 160 KiB of K plus 160 KiB of V per block) copied from
+    HBM to pinned host memory and back with pa_swap_blocks, scattered block IDs on
+    both sides.  A plain contiguous copy of the same bytes (DMA engine) is timed
+    beside it as the link's achievable rate."""
+    import torch
+    from paged_kv_cache_397_amd import ops, _native
+    from paged_kv_cache_397_amd.allocator import BlockAllocator
+    from workloads import gen
+
+    _native.lib()
+    nblk, nswap = 4096, 1024
+    spec = ops.CacheSpec(nblk, 16, 40, 128, "bf16")
+    kc, vc = ops.empty_cache(spec)
+    kc.normal_()
+    vc.normal_()
+    hk, hv = ops.host_pool(spec, nswap)
+    alloc = BlockAllocator(nblk, 16, gen.pool_permutation(12, nblk))
+    alloc.set_host_pool(nswap)
+    alloc.add(0, nswap * 16)
+    out_pairs = torch.from_numpy(alloc.swap_out(0)).cuda()
+    in_pairs = torch.from_numpy(alloc.swap_in(0)).cuda()
+    nbytes = nswap * 2 * spec.num_kv_heads * spec.block_size * spec.head_dim * 2
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    reps = max(args.steps // 10, 3)
+    t_out = timed(lambda: ops.swap_blocks(spec, kc, vc, hk, hv, out_pairs), reps)
+    t_in = timed(lambda: ops.swap_blocks(spec, hk, hv, kc, vc, in_pairs), reps)
+    dma_host = torch.empty(nbytes // 2, dtype=torch.bfloat16, pin_memory=True)
+    dma_dev = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    t_dma_out = timed(lambda: dma_host.copy_(dma_dev, non_blocking=True), reps)
+    t_dma_in = timed(lambda: dma_dev.copy_(dma_host, non_blocking=True), reps)
+    gbps_out, gbps_in = nbytes / t_out / 1e9, nbytes / t_in / 1e9
+    result = {
+        "metric": "swap preemption: HBM <-> pinned host block copy GB/s",
+        "value": round(min(gbps_out, gbps_in), 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": 1,
+        "ms_per_step": round((t_out + t_in) * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "swap_13b: 1024 scattered blocks (40x16x128 bf16, K+V 320 KiB each) "
+                               "out to pinned host memory and back", "bytes_per_direction": nbytes},
+        "swap_out_gbps": round(gbps_out, 2),
+        "swap_in_gbps": round(gbps_in, 2),
+        "dma_contiguous_gbps": {"device_to_host": round(nbytes / t_dma_out / 1e9, 2),
+                                "host_to_device": round(nbytes / t_dma_in / 1e9, 2)},
+        "roofline": {"kernel": "swap_blocks_kernel", "bound": "pcie", "achieved": round(min(gbps_out, gbps_in), 2),
+                     "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(min(gbps_out, gbps_in) / PCIE_PEAK_GBPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        from oracle.cache import swap_blocks as oracle_swap
+        from oracle.layout import CacheLayout
+        lay = CacheLayout(64, 40, 16, 128, "bf16")
+        src = np.zeros(lay.cache_elems, dtype=np.uint16)
+        dst = np.zeros_like(src)
+        pairs = np.stack([np.arange(64), np.arange(64)[::-1]], axis=1)
+        times = []
+        t_end = time.perf_counter() + min(args.cpu_seconds, 5.0)
+        while not times or time.perf_counter() < t_end:
+            t0 = time.perf_counter()
+            oracle_swap(lay, src, src, lay, dst, dst, pairs)
+            times.append(time.perf_counter() - t0)
+        b = 64 * 2 * lay.block_elems() * 2
+        result["cpu_baseline"] = {"value": round(b / float(np.median(times)) / 1e9, 2), "unit": "GB/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": "oracle whole-block copy of 64 blocks between two host pools"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -465,6 +558,9 @@ def main():
         return
     if args.config.startswith("prefill"):
         run_prefill(args)
+        return
+    if args.config == "swap_13b":
+        run_swap(args)
         return
     import torch
     from paged_kv_cache_397_amd import ops, _native

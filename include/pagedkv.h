@@ -263,6 +263,21 @@ pa_status pa_paged_attn_prefill(const pa_cache_desc* desc, void* out, const void
                                 void* stream);
 
 /*
+ * Whole-block copies between two pools of the same block geometry (desc's
+ * num_kv_heads, block_size, head_dim, dtype; desc->num_blocks is not used):
+ * for k < num_pairs, block pairs[2k] of (src_k, src_v), a pool of src_blocks
+ * blocks, is copied onto block pairs[2k+1] of (dst_k, dst_v), a pool of
+ * dst_blocks blocks.  Either pool may be device memory or pinned host memory
+ * (hipHostMalloc / torch pin_memory); pairs may be device or pinned host
+ * memory.  Pairs naming a block outside its pool are skipped.  Destination
+ * blocks must be distinct and must not be sources of the same call.  This is
+ * the data half of swapping (pa_seq_swap_out / pa_seq_swap_in give the pairs).
+ */
+pa_status pa_swap_blocks(const pa_cache_desc* desc, const void* src_k, const void* src_v,
+                         int32_t src_blocks, void* dst_k, void* dst_v, int32_t dst_blocks,
+                         const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/*
  * Host block allocator ("block manager", [P1] section 2.2; sample structure in
  * [P3] section 2.2).  Host memory only; not thread-safe; one instance per
  * cache.  Semantics:
@@ -354,6 +369,38 @@ pa_status pa_seq_add_prefix(pa_allocator* a, int64_t seq, const int32_t* tokens,
                             int32_t num_tokens, int32_t* num_cached_tokens);
 pa_status pa_seq_register_blocks(pa_allocator* a, int64_t seq, const int32_t* tokens,
                                  int32_t num_tokens);
+/*
+ * Swapping ([P2] Preemption（抢占）: Recompute or Swap, "move the KV cache to the
+ * CPU"; [P1] section 3.4 on --swap-space).  A host pool of num_host_blocks
+ * blocks (its own FIFO queue, IDs 0..n-1, initially empty pool) holds swapped
+ * sequences; the caller owns the host memory and copies with pa_swap_blocks.
+ *   - set_host_pool: (re)size the host pool; PA_ERR_STATE while any sequence is
+ *     swapped out;
+ *   - swap_out(seq): all-or-nothing; takes one host block per table entry from
+ *     the host queue's head and writes (device block, host block) pairs in
+ *     logical order into pairs[2k], pairs[2k+1]; the device references are
+ *     dropped as in free (a shared block stays for its other holders).  The
+ *     sequence keeps its length and prefix-cache progress;
+ *   - swap_in(seq): all-or-nothing; fresh device blocks from the queue's head
+ *     (evicting cached blocks as any allocation does), (host block, device
+ *     block) pairs in logical order; the host blocks return to the host queue's
+ *     tail in logical order;
+ *   - a swapped sequence accepts only swap_in, free (its host blocks return),
+ *     seq_info and is_swapped; everything else returns PA_ERR_STATE.
+ * PA_ERR_INVALID_ARG when cap is below the sequence's block count.
+ */
+pa_status pa_alloc_set_host_pool(pa_allocator* a, int32_t num_host_blocks);
+int32_t   pa_alloc_num_free_host(const pa_allocator* a);             /* -1 if a == NULL */
+/* Copy the host queue, head first, into out[0..cap); *n = its full length. */
+pa_status pa_alloc_host_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n);
+/* A swapped sequence's host blocks in logical order (PA_ERR_STATE if not swapped). */
+pa_status pa_seq_host_blocks(const pa_allocator* a, int64_t seq, int32_t* out, int32_t cap);
+int32_t   pa_seq_is_swapped(const pa_allocator* a, int64_t seq);     /* 1, 0, or -1 if unknown */
+pa_status pa_seq_swap_out(pa_allocator* a, int64_t seq, int32_t* pairs, int32_t cap,
+                          int32_t* num_pairs);
+pa_status pa_seq_swap_in(pa_allocator* a, int64_t seq, int32_t* pairs, int32_t cap,
+                         int32_t* num_pairs);
+
 /* Blocks looked up and reused by add_prefix so far, and blocks cached now. */
 pa_status pa_alloc_prefix_stats(const pa_allocator* a, int64_t* lookups, int64_t* hits,
                                 int32_t* cached_blocks);

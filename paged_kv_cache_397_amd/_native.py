@@ -74,6 +74,14 @@ SIGNATURES = {
     "pa_seq_register_blocks": (c_i32, [c_vp, c_i64, c_vp, c_i32]),
     "pa_alloc_prefix_stats": (c_i32, [c_vp, P_i64, P_i64, P_i32]),
     "pa_alloc_block_cached": (c_i32, [c_vp, c_i32, ctypes.POINTER(ctypes.c_uint64)]),
+    "pa_swap_blocks": (c_i32, [P_desc, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
+    "pa_alloc_set_host_pool": (c_i32, [c_vp, c_i32]),
+    "pa_alloc_num_free_host": (c_i32, [c_vp]),
+    "pa_alloc_host_free_list": (c_i32, [c_vp, c_vp, c_i32, P_i32]),
+    "pa_seq_host_blocks": (c_i32, [c_vp, c_i64, c_vp, c_i32]),
+    "pa_seq_is_swapped": (c_i32, [c_vp, c_i64]),
+    "pa_seq_swap_out": (c_i32, [c_vp, c_i64, c_vp, c_i32, P_i32]),
+    "pa_seq_swap_in": (c_i32, [c_vp, c_i64, c_vp, c_i32, P_i32]),
 }
 
 _lib = None

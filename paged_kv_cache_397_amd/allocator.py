@@ -157,3 +157,45 @@ class BlockAllocator:
             if self._lib.pa_alloc_block_cached(self._h, b, ctypes.byref(key)) == 1:
                 out[b] = key.value
         return out
+
+    # -- swapping -------------------------------------------------------------
+    def set_host_pool(self, num_host_blocks: int) -> None:
+        N.check(self._lib.pa_alloc_set_host_pool(self._h, num_host_blocks), "alloc_set_host_pool")
+
+    def num_free_host(self) -> int:
+        return int(self._lib.pa_alloc_num_free_host(self._h))
+
+    def host_free_list(self) -> list[int]:
+        n = ctypes.c_int32()
+        N.check(self._lib.pa_alloc_host_free_list(self._h, None, 0, ctypes.byref(n)), "host_free_list")
+        out = np.empty(max(n.value, 1), dtype=np.int32)
+        N.check(self._lib.pa_alloc_host_free_list(self._h, _ptr(out), n.value, ctypes.byref(n)),
+                "host_free_list")
+        return out[:n.value].tolist()
+
+    def host_blocks(self, seq: int) -> list[int]:
+        _, nb = self.info(seq)
+        out = np.empty(max(nb, 1), dtype=np.int32)
+        N.check(self._lib.pa_seq_host_blocks(self._h, seq, _ptr(out), nb), "seq_host_blocks")
+        return out[:nb].tolist()
+
+    def is_swapped(self, seq: int) -> bool:
+        r = int(self._lib.pa_seq_is_swapped(self._h, seq))
+        if r < 0:
+            raise N.PagedKVError(N.PA_ERR_STATE, "seq_is_swapped")
+        return bool(r)
+
+    def _swap(self, fn: str, seq: int) -> np.ndarray:
+        _, nb = self.info(seq)
+        pairs = np.empty((max(nb, 1), 2), dtype=np.int32)
+        n = ctypes.c_int32()
+        N.check(getattr(self._lib, fn)(self._h, seq, _ptr(pairs), nb, ctypes.byref(n)), fn)
+        return pairs[:n.value]
+
+    def swap_out(self, seq: int) -> np.ndarray:
+        """Move the sequence to host blocks; returns (device, host) block pairs [n, 2]."""
+        return self._swap("pa_seq_swap_out", seq)
+
+    def swap_in(self, seq: int) -> np.ndarray:
+        """Bring the sequence back; returns (host, device) block pairs [n, 2]."""
+        return self._swap("pa_seq_swap_in", seq)

@@ -19,10 +19,16 @@
 // it from the head (eviction).  Hits may leave the middle of the queue, so the
 // queue is a doubly linked list over block IDs.
 //
+// Swapping (hihuo.com page, Preemption（抢占）: the Recompute and Swap modes;
+// ksqn.cn page, 3.4 on --swap-space): a suspended sequence's blocks move to a
+// host pool with its own FIFO queue and come back later onto fresh device blocks;
+// the caller copies the data with pa_swap_blocks.
+//
 // Plain C++17, no HIP: this file also builds with g++ alone.
 
 #include <cstdint>
 #include <cstring>
+#include <deque>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -58,6 +64,7 @@ struct pa_allocator {
         int32_t len = 0;
         int32_t reg_done = 0;   // leading full blocks already offered to the prefix cache
         uint64_t reg_hash = 0;  // chain key after them
+        bool swapped = false;   // table holds host blocks
     };
     int32_t num_blocks = 0;
     int32_t block_size = 0;
@@ -72,6 +79,19 @@ struct pa_allocator {
     std::vector<uint64_t> key;                     // block -> key, when is_cached
     std::vector<char> is_cached;
     int64_t lookups = 0, hits = 0;
+    // host pool for swapped sequences (FIFO)
+    int32_t num_host_blocks = 0;
+    std::deque<int32_t> host_free;
+
+    // A resident (not swapped) sequence, or nullptr.
+    Seq* resident(int64_t id) {
+        auto it = seqs.find(id);
+        return (it == seqs.end() || it->second.swapped) ? nullptr : &it->second;
+    }
+    const Seq* resident(int64_t id) const {
+        auto it = seqs.find(id);
+        return (it == seqs.end() || it->second.swapped) ? nullptr : &it->second;
+    }
 
     void push_back(int32_t b) {
         prev[b] = tail;
@@ -105,9 +125,9 @@ struct pa_allocator {
     // Reserve the slot of seq's next token; see pa_seq_append.
     pa_status append(int64_t id, int64_t* slot, int32_t* cow_src, int32_t* cow_dst,
                      int32_t* new_block, int32_t* new_col) {
-        auto it = seqs.find(id);
-        if (it == seqs.end()) return PA_ERR_STATE;
-        Seq& s = it->second;
+        Seq* sp = resident(id);
+        if (!sp) return PA_ERR_STATE;
+        Seq& s = *sp;
         const int32_t pos = s.len;
         const int32_t j = pos / block_size;
         int32_t src = -1, dst = -1, fresh = -1;
@@ -240,9 +260,9 @@ pa_status pa_seq_add_prefix(pa_allocator* a, int64_t seq, const int32_t* tokens,
 pa_status pa_seq_register_blocks(pa_allocator* a, int64_t seq, const int32_t* tokens,
                                  int32_t num_tokens) {
     if (!a || num_tokens < 0 || (num_tokens > 0 && !tokens)) return PA_ERR_INVALID_ARG;
-    auto it = a->seqs.find(seq);
-    if (it == a->seqs.end()) return PA_ERR_STATE;
-    pa_allocator::Seq& s = it->second;
+    pa_allocator::Seq* sp = a->resident(seq);
+    if (!sp) return PA_ERR_STATE;
+    pa_allocator::Seq& s = *sp;
     if (num_tokens > s.len) return PA_ERR_INVALID_ARG;
     const int32_t B = a->block_size;
     for (int32_t i = s.reg_done; i < num_tokens / B; ++i) {
@@ -298,9 +318,9 @@ pa_status pa_seq_append_batch(pa_allocator* a, const int64_t* seqs, int32_t n, i
 
 pa_status pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child) {
     if (!a) return PA_ERR_INVALID_ARG;
-    auto it = a->seqs.find(parent);
-    if (it == a->seqs.end() || a->seqs.count(child)) return PA_ERR_STATE;
-    pa_allocator::Seq c = it->second;
+    const pa_allocator::Seq* p = a->resident(parent);
+    if (!p || a->seqs.count(child)) return PA_ERR_STATE;
+    pa_allocator::Seq c = *p;
     for (int32_t b : c.table) a->ref[b] += 1;
     a->seqs.emplace(child, std::move(c));
     return PA_OK;
@@ -310,7 +330,11 @@ pa_status pa_seq_free(pa_allocator* a, int64_t seq) {
     if (!a) return PA_ERR_INVALID_ARG;
     auto it = a->seqs.find(seq);
     if (it == a->seqs.end()) return PA_ERR_STATE;
-    for (int32_t b : it->second.table) a->release_block(b);
+    if (it->second.swapped) {
+        for (int32_t h : it->second.table) a->host_free.push_back(h);
+    } else {
+        for (int32_t b : it->second.table) a->release_block(b);
+    }
     a->seqs.erase(it);
     return PA_OK;
 }
@@ -318,9 +342,9 @@ pa_status pa_seq_free(pa_allocator* a, int64_t seq) {
 pa_status pa_seq_slots(const pa_allocator* a, int64_t seq, int32_t start, int32_t count,
                        int64_t* out) {
     if (!a || start < 0 || count < 0 || (count > 0 && !out)) return PA_ERR_INVALID_ARG;
-    auto it = a->seqs.find(seq);
-    if (it == a->seqs.end()) return PA_ERR_STATE;
-    const auto& s = it->second;
+    const pa_allocator::Seq* sp = a->resident(seq);
+    if (!sp) return PA_ERR_STATE;
+    const auto& s = *sp;
     if (static_cast<int64_t>(start) + count > s.len) return PA_ERR_INVALID_ARG;
     const int32_t B = a->block_size;
     for (int32_t k = 0; k < count; ++k) {
@@ -342,9 +366,9 @@ pa_status pa_seq_info(const pa_allocator* a, int64_t seq, int32_t* num_tokens,
 
 pa_status pa_seq_block_table(const pa_allocator* a, int64_t seq, int32_t* out, int32_t cap) {
     if (!a || cap < 0 || (cap > 0 && !out)) return PA_ERR_INVALID_ARG;
-    auto it = a->seqs.find(seq);
-    if (it == a->seqs.end()) return PA_ERR_STATE;
-    const auto& t = it->second.table;
+    const pa_allocator::Seq* sp = a->resident(seq);
+    if (!sp) return PA_ERR_STATE;
+    const auto& t = sp->table;
     if (static_cast<int64_t>(t.size()) > cap) return PA_ERR_INVALID_ARG;
     if (!t.empty()) std::memcpy(out, t.data(), t.size() * sizeof(int32_t));
     return PA_OK;
@@ -357,10 +381,9 @@ pa_status pa_batch_metadata(const pa_allocator* a, const int64_t* seqs, int32_t 
         (n > 0 && (!seqs || !context_lens || (max_blocks_per_seq > 0 && !block_tables))))
         return PA_ERR_INVALID_ARG;
     for (int32_t k = 0; k < n; ++k) {
-        auto it = a->seqs.find(seqs[k]);
-        if (it == a->seqs.end()) return PA_ERR_STATE;
-        if (static_cast<int64_t>(it->second.table.size()) > max_blocks_per_seq)
-            return PA_ERR_INVALID_ARG;
+        const pa_allocator::Seq* sp = a->resident(seqs[k]);
+        if (!sp) return PA_ERR_STATE;
+        if (static_cast<int64_t>(sp->table.size()) > max_blocks_per_seq) return PA_ERR_INVALID_ARG;
     }
     for (int32_t k = 0; k < n; ++k) {
         const auto& s = a->seqs.find(seqs[k])->second;
@@ -370,6 +393,89 @@ pa_status pa_batch_metadata(const pa_allocator* a, const int64_t* seqs, int32_t 
         for (int32_t c = nb; c < max_blocks_per_seq; ++c) row[c] = -1;
         context_lens[k] = s.len;
     }
+    return PA_OK;
+}
+
+pa_status pa_alloc_set_host_pool(pa_allocator* a, int32_t num_host_blocks) {
+    if (!a || num_host_blocks < 0) return PA_ERR_INVALID_ARG;
+    for (const auto& kv : a->seqs)
+        if (kv.second.swapped) return PA_ERR_STATE;
+    a->num_host_blocks = num_host_blocks;
+    a->host_free.clear();
+    for (int32_t h = 0; h < num_host_blocks; ++h) a->host_free.push_back(h);
+    return PA_OK;
+}
+
+pa_status pa_alloc_host_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n) {
+    if (!a || !n || cap < 0 || (cap > 0 && !out)) return PA_ERR_INVALID_ARG;
+    *n = static_cast<int32_t>(a->host_free.size());
+    int32_t k = 0;
+    for (auto it = a->host_free.begin(); it != a->host_free.end() && k < cap; ++it) out[k++] = *it;
+    return PA_OK;
+}
+
+pa_status pa_seq_host_blocks(const pa_allocator* a, int64_t seq, int32_t* out, int32_t cap) {
+    if (!a || cap < 0 || (cap > 0 && !out)) return PA_ERR_INVALID_ARG;
+    auto it = a->seqs.find(seq);
+    if (it == a->seqs.end() || !it->second.swapped) return PA_ERR_STATE;
+    const auto& t = it->second.table;
+    if (static_cast<int64_t>(t.size()) > cap) return PA_ERR_INVALID_ARG;
+    if (!t.empty()) std::memcpy(out, t.data(), t.size() * sizeof(int32_t));
+    return PA_OK;
+}
+
+int32_t pa_alloc_num_free_host(const pa_allocator* a) {
+    return a ? static_cast<int32_t>(a->host_free.size()) : -1;
+}
+
+int32_t pa_seq_is_swapped(const pa_allocator* a, int64_t seq) {
+    if (!a) return -1;
+    auto it = a->seqs.find(seq);
+    if (it == a->seqs.end()) return -1;
+    return it->second.swapped ? 1 : 0;
+}
+
+pa_status pa_seq_swap_out(pa_allocator* a, int64_t seq, int32_t* pairs, int32_t cap,
+                          int32_t* num_pairs) {
+    if (!a || cap < 0 || (cap > 0 && !pairs) || !num_pairs) return PA_ERR_INVALID_ARG;
+    pa_allocator::Seq* sp = a->resident(seq);
+    if (!sp) return PA_ERR_STATE;
+    const int32_t n = static_cast<int32_t>(sp->table.size());
+    if (n > cap) return PA_ERR_INVALID_ARG;
+    if (n > static_cast<int32_t>(a->host_free.size())) return PA_ERR_OOM;
+    for (int32_t k = 0; k < n; ++k) {
+        const int32_t b = sp->table[k];
+        const int32_t h = a->host_free.front();
+        a->host_free.pop_front();
+        pairs[2 * k] = b;
+        pairs[2 * k + 1] = h;
+        sp->table[k] = h;
+        a->release_block(b);
+    }
+    sp->swapped = true;
+    *num_pairs = n;
+    return PA_OK;
+}
+
+pa_status pa_seq_swap_in(pa_allocator* a, int64_t seq, int32_t* pairs, int32_t cap,
+                         int32_t* num_pairs) {
+    if (!a || cap < 0 || (cap > 0 && !pairs) || !num_pairs) return PA_ERR_INVALID_ARG;
+    auto it = a->seqs.find(seq);
+    if (it == a->seqs.end() || !it->second.swapped) return PA_ERR_STATE;
+    pa_allocator::Seq& s = it->second;
+    const int32_t n = static_cast<int32_t>(s.table.size());
+    if (n > cap) return PA_ERR_INVALID_ARG;
+    if (n > a->nfree) return PA_ERR_OOM;
+    for (int32_t k = 0; k < n; ++k) {
+        const int32_t h = s.table[k];
+        const int32_t b = a->take();
+        pairs[2 * k] = h;
+        pairs[2 * k + 1] = b;
+        s.table[k] = b;
+        a->host_free.push_back(h);
+    }
+    s.swapped = false;
+    *num_pairs = n;
     return PA_OK;
 }
 

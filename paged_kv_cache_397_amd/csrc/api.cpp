@@ -119,6 +119,23 @@ pa_status pa_copy_blocks(const pa_cache_desc* d, void* k_cache, void* v_cache,
                                             static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_swap_blocks(const pa_cache_desc* d, const void* src_k, const void* src_v,
+                         int32_t src_blocks, void* dst_k, void* dst_v, int32_t dst_blocks,
+                         const int32_t* pairs, int32_t num_pairs, void* stream) {
+    pa_status st = check_desc(d);
+    if (st != PA_OK) return st;
+    if (num_pairs < 0 || src_blocks < 0 || dst_blocks < 0) return PA_ERR_INVALID_ARG;
+    if (num_pairs == 0) return PA_OK;
+    if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PA_ERR_INVALID_ARG;
+    if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 16) || !aligned(dst_v, 16) ||
+        !aligned(pairs, 4))
+        return PA_ERR_INVALID_ARG;
+    if (num_pairs > 2147483647 / 2) return PA_ERR_UNSUPPORTED;
+    return from_hip(pkv::launch_swap_blocks(d->dtype, d->head_dim, d->block_size, d->num_kv_heads,
+                                            src_k, src_v, src_blocks, dst_k, dst_v, dst_blocks,
+                                            pairs, num_pairs, static_cast<hipStream_t>(stream)));
+}
+
 pa_status pa_append_tokens(const pa_cache_desc* d, const void* k, const void* v,
                            const int64_t* slot_mapping, const int32_t* cow_pairs,
                            int32_t num_tokens, void* k_cache, void* v_cache,

@@ -67,6 +67,38 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_
     }
 }
 
+// Whole-block copies between two pools of the same block geometry - HBM and pinned
+// host memory for swapping a suspended sequence out and back (hihuo.com "vLLM 原理：
+// PagedAttention 和 Continuous Batching", Preemption（抢占）: the Swap mode).  A block
+// is one contiguous region of each cache array; workgroup (pair, K or V, chunk)
+// moves 16 KiB with four 16-B loads in flight per thread, so that many requests
+// cross the host link at once.  Pairs naming a block outside its pool are skipped.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(const u32x4* __restrict__ src_k,
+                                                          const u32x4* __restrict__ src_v,
+                                                          u32x4* __restrict__ dst_k,
+                                                          u32x4* __restrict__ dst_v,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int src_blocks, int dst_blocks,
+                                                          int64_t block_u4) {
+    const int src = pairs[2 * blockIdx.x];
+    const int dst = pairs[2 * blockIdx.x + 1];
+    if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+    const u32x4* s = (blockIdx.y == 0 ? src_k : src_v) + src * block_u4;
+    u32x4* d = (blockIdx.y == 0 ? dst_k : dst_v) + dst * block_u4;
+    const int64_t n = static_cast<int64_t>(blockIdx.z) * 1024 + threadIdx.x;
+    u32x4 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t idx = n + k * 256;
+        if (idx < block_u4) r[k] = s[idx];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t idx = n + k * 256;
+        if (idx < block_u4) d[idx] = r[k];
+    }
+}
+
 __global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict__ tables, int rows,
                                                             int cols,
                                                             const int32_t* __restrict__ upd,
@@ -220,6 +252,20 @@ hipError_t launch_copy_blocks(int dtype, int head_dim, int block_size, int num_k
     hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream,
                        static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), pairs,
                        num_blocks, block_u4);
+    return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(int dtype, int head_dim, int block_size, int num_kv_heads,
+                              const void* src_k, const void* src_v, int src_blocks, void* dst_k,
+                              void* dst_v, int dst_blocks, const int32_t* pairs, int num_pairs,
+                              hipStream_t stream) {
+    const int64_t block_u4 = static_cast<int64_t>(num_kv_heads) * block_size * head_dim *
+                             (dtype == 0 ? 4 : 2) / 16;
+    const dim3 grid(num_pairs, 2, static_cast<unsigned>((block_u4 + 1023) / 1024));
+    hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src_k), static_cast<const u32x4*>(src_v),
+                       static_cast<u32x4*>(dst_k), static_cast<u32x4*>(dst_v), pairs, src_blocks,
+                       dst_blocks, block_u4);
     return hipGetLastError();
 }
 

@@ -74,6 +74,10 @@ hipError_t launch_append_tokens(int dtype, int head_dim, int block_size, int num
 hipError_t launch_copy_blocks(int dtype, int head_dim, int block_size, int num_kv_heads,
                               int num_blocks, void* k_cache, void* v_cache, const int32_t* pairs,
                               int num_pairs, hipStream_t stream);
+hipError_t launch_swap_blocks(int dtype, int head_dim, int block_size, int num_kv_heads,
+                              const void* src_k, const void* src_v, int src_blocks, void* dst_k,
+                              void* dst_v, int dst_blocks, const int32_t* pairs, int num_pairs,
+                              hipStream_t stream);
 hipError_t launch_update_block_tables(int32_t* tables, int rows, int cols, const int32_t* upd,
                                       int n, hipStream_t stream);
 // passes: bit 0 = pass 1 (tiles -> outputs / partial records), bit 1 = pass 2 (merge).

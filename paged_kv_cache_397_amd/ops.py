@@ -102,6 +102,26 @@ def copy_blocks(spec: CacheSpec, k_cache, v_cache, pairs, stream=None):
     N.check(st, "pa_copy_blocks")
 
 
+def host_pool(spec: CacheSpec, num_blocks: int):
+    """Pinned host K and V arrays for a swap pool of num_blocks blocks of spec's geometry."""
+    n = num_blocks * spec.num_kv_heads * spec.block_size * spec.head_dim
+    return (torch.empty(n, dtype=spec.torch_dtype, pin_memory=True),
+            torch.empty(n, dtype=spec.torch_dtype, pin_memory=True))
+
+
+def swap_blocks(spec: CacheSpec, src_k, src_v, dst_k, dst_v, pairs, stream=None):
+    """Copy block pairs[i, 0] of (src_k, src_v) onto block pairs[i, 1] of (dst_k, dst_v);
+    either pool may be a GPU tensor or pinned host memory, as may pairs ([n, 2] int32)."""
+    n = pairs.shape[0] if pairs.dim() == 2 else pairs.numel() // 2
+    per = spec.num_kv_heads * spec.block_size * spec.head_dim
+    st = N.lib().pa_swap_blocks(
+        ctypes.byref(spec.desc()), _acc(src_k, "src_k", spec.torch_dtype),
+        _acc(src_v, "src_v", spec.torch_dtype), src_k.numel() // per,
+        _acc(dst_k, "dst_k", spec.torch_dtype), _acc(dst_v, "dst_v", spec.torch_dtype),
+        dst_k.numel() // per, _acc(pairs, "pairs", torch.int32), n, _stream(stream))
+    N.check(st, "pa_swap_blocks")
+
+
 def _append_args(spec, k, v, slot_mapping, k_cache, v_cache, cow_pairs, block_tables,
                  table_updates, lens_in, lens_out, stream):
     T = slot_mapping.numel()
