@@ -44,6 +44,15 @@ Readings where the pages are silent (the library's scheduler takes the same):
   plus the tokens it generated, so its own cached blocks can serve the
   recompute.
 
+* With a host pool (swap preemption, hihuo.com page, Preemption（抢占）: Swap),
+  the preempted request is swapped out instead of released when the host pool
+  can hold it (else it is recomputed as above); it keeps its progress.  Swapped
+  requests come back first, in swap-out order, each step before any admission;
+  while one of them does not fit, no new request is admitted.  A request swapped
+  back in rejoins the running list at its end.  The step's device work runs in
+  the order: swap-in copies, prompt writes and prefill, swap-out copies (so that
+  a chunk written this step travels with its request), decode writes and decode.
+
 Pins: a hand-worked trace on a four-block pool (tests/test_scheduler.py) that
 exercises admission, chunking, release, head-of-line blocking, and preemption
 of another request and of the requester itself; conservation of blocks after
@@ -83,14 +92,20 @@ class StepRecord:
     preempted: list = field(default_factory=list)
     decode: list = field(default_factory=list)       # (rid, position, slot, cow)
     cached: list = field(default_factory=list)       # (rid, cached prompt tokens) per admission
+    swapped_in: list = field(default_factory=list)   # (rid, [(host, device) block pairs])
+    swapped_out: list = field(default_factory=list)  # (rid, [(device, host) block pairs])
 
 
 class SchedulerModel:
     def __init__(self, num_blocks: int, block_size: int, chunk: int, initial_free_order=None,
-                 gen_token=None):
+                 gen_token=None, num_host_blocks: int = 0):
         """gen_token(rid, position) -> token ID turns prefix caching on; arrivals
-        then carry (prompt token IDs, out_len)."""
-        self.alloc = AllocatorModel(num_blocks, block_size, initial_free_order)
+        then carry (prompt token IDs, out_len).  num_host_blocks > 0 turns swap
+        preemption on."""
+        self.alloc = AllocatorModel(num_blocks, block_size, initial_free_order,
+                                    num_host_blocks=num_host_blocks)
+        self.swap = num_host_blocks > 0
+        self.swapped_q: deque[Request] = deque()
         self.gen_token = gen_token
         self.B = block_size
         self.chunk = chunk
@@ -118,8 +133,18 @@ class SchedulerModel:
             self.next_rid += 1
             self.waiting.append(r)
             rec.arrived.append(r.rid)
-        # 2b. admit first come, first served while the whole prompt fits
-        while self.waiting:
+        # 2b. swapped requests come back first, in swap-out order
+        while self.swapped_q:
+            r = self.swapped_q[0]
+            try:
+                pairs = self.alloc.swap_in(r.rid)
+            except OutOfBlocks:
+                break
+            self.swapped_q.popleft()
+            self.running.append(r)
+            rec.swapped_in.append((r.rid, pairs))
+        # 2c. admit first come, first served while the whole prompt fits
+        while self.waiting and not self.swapped_q:
             r = self.waiting[0]
             if prefix:
                 try:
@@ -154,6 +179,11 @@ class SchedulerModel:
                     slot, cow = self.alloc.append(r.rid)
                 except OutOfBlocks:
                     victim = self.running[-1]
+                    if self.swap and len(self.alloc.block_table(victim.rid)) <= len(self.alloc.host_free):
+                        rec.swapped_out.append((victim.rid, self.alloc.swap_out(victim.rid)))
+                        self.running.remove(victim)
+                        self.swapped_q.append(victim)
+                        continue
                     self.alloc.release(victim.rid)
                     self.running.remove(victim)
                     victim.prompt_eff = victim.prompt + victim.generated

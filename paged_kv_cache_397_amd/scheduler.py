@@ -22,6 +22,12 @@ IDs; admission reuses the cached opening of each prompt through the allocator's
 planned chunk's full blocks are registered, and after the decode appends every
 decoding request's newly full blocks are registered, in admission order.
 
+With a host pool (``num_host_blocks`` > 0) a preempted request is swapped out
+when the pool can hold it (hihuo.com page, Preemption（抢占）: Swap), else
+recomputed; swapped requests come back first, in swap-out order, before any new
+admission.  The caller runs a step's device work in the order: swap-in copies,
+prompt writes and prefill, swap-out copies, decode writes and decode.
+
 The plan a step returns says which slots to write and which sequences to decode;
 the caller performs the device work (cache writes, then attention).
 """
@@ -70,6 +76,8 @@ class StepPlan:
     decode_slots: np.ndarray = None               # int64[n]
     decode_cows: np.ndarray = None                # int32[n, 2], -1 = no copy
     cached: list = field(default_factory=list)    # (rid, cached prompt tokens) per admission
+    swapped_in: list = field(default_factory=list)   # (rid, int32[n, 2] (host, device) pairs)
+    swapped_out: list = field(default_factory=list)  # (rid, int32[n, 2] (device, host) pairs)
 
     def prefill_tokens(self) -> int:
         return sum(c for _, _, c, _ in self.prefill)
@@ -77,10 +85,15 @@ class StepPlan:
 
 class TraceScheduler:
     def __init__(self, num_blocks: int, block_size: int, chunk: int, initial_free_order=None,
-                 gen_token=None):
+                 gen_token=None, num_host_blocks: int = 0):
         """gen_token(rid, position) -> token ID turns prefix caching on; arrivals
-        then carry (prompt token IDs, out_len)."""
+        then carry (prompt token IDs, out_len).  num_host_blocks > 0 turns swap
+        preemption on."""
         self.alloc = BlockAllocator(num_blocks, block_size, initial_free_order)
+        self.swap = num_host_blocks > 0
+        if self.swap:
+            self.alloc.set_host_pool(num_host_blocks)
+        self.swapped_q: deque[_Req] = deque()
         self.gen_token = gen_token
         self.B = block_size
         self.chunk = chunk
@@ -114,7 +127,18 @@ class TraceScheduler:
             self.next_rid += 1
             self.waiting.append(r)
             plan.arrived.append(r.rid)
-        while self.waiting:
+        while self.swapped_q:
+            r = self.swapped_q[0]
+            try:
+                pairs = alloc.swap_in(r.rid)
+            except N.PagedKVError as e:
+                if e.status != N.PA_ERR_OOM:
+                    raise
+                break
+            self.swapped_q.popleft()
+            self.running.append(r)
+            plan.swapped_in.append((r.rid, pairs))
+        while self.waiting and not self.swapped_q:
             r = self.waiting[0]
             if prefix:
                 try:
@@ -163,6 +187,11 @@ class TraceScheduler:
                 N.check(st, "seq_append_batch")
             # out of blocks at pending[done]: preempt the youngest running request
             victim = self.running.pop()
+            if self.swap and alloc.info(victim.rid)[1] <= alloc.num_free_host():
+                plan.swapped_out.append((victim.rid, alloc.swap_out(victim.rid)))
+                self.swapped_q.append(victim)
+                pending = [r for r in pending[done:] if r is not victim]
+                continue
             alloc.free(victim.rid)
             victim.prompt_eff = victim.prompt + victim.generated
             victim.prefilled = 0

@@ -71,3 +71,70 @@ def test_trace_decode_matches_oracle(Hq, Hkv):
         decoded += S
     assert preempted > 0, "the small pool was meant to force preemption"
     assert decoded > 300
+
+
+def test_trace_with_swap_preemption_matches_oracle():
+    """The same trace with a host pool: victims are swapped out to pinned host memory
+    and back instead of recomputed.  Each step runs swap-in copies, prompt writes,
+    swap-out copies, then decode writes and decode attention, checked against the
+    oracle on every decoded sequence."""
+    cfg = CONFIGS["trace_small"]
+    B, D, dtype, Hq, Hkv = cfg.block_size, cfg.head_dim, cfg.dtype, 8, 4
+    spec = ops.CacheSpec(cfg.num_blocks, B, Hkv, D, dtype)
+    kc, vc = ops.empty_cache(spec)
+    kc.fill_(float("nan"))
+    vc.fill_(float("nan"))
+    host = 120
+    hk, hv = ops.host_pool(spec, host)
+    sched = TraceScheduler(cfg.num_blocks, B, cfg.chunk, gen.pool_permutation(cfg.seed, cfg.num_blocks),
+                           num_host_blocks=host)
+    max_blocks = -(-(cfg.prompt_hi + cfg.out_hi) // B)
+    scale = 1 / math.sqrt(D)
+    swapped = swapped_back = decoded = 0
+
+    def pairs_of(lst):
+        return torch.from_numpy(np.ascontiguousarray(np.concatenate([p for _, p in lst]))).cuda()
+
+    for n in range(cfg.steps):
+        p, o = gen.trace_arrivals(cfg.seed, n, cfg.arrival_mean, cfg.prompt_lo, cfg.prompt_hi,
+                                  cfg.out_p, cfg.out_lo, cfg.out_hi)
+        plan = sched.step(n, list(zip(p.tolist(), o.tolist())))
+        if plan.swapped_in:
+            ops.swap_blocks(spec, hk, hv, kc, vc, pairs_of(plan.swapped_in))
+            swapped_back += len(plan.swapped_in)
+        if plan.prefill:
+            ks, vs, sl = [], [], []
+            for rid, start, count, slots in plan.prefill:
+                k, v = gen.trace_token_kv(cfg.seed, rid, range(start, start + count), Hkv, D, dtype)
+                ks.append(k), vs.append(v), sl.append(slots)
+            ops.reshape_and_cache(spec, to_device(np.concatenate(ks), spec),
+                                  to_device(np.concatenate(vs), spec),
+                                  torch.from_numpy(np.concatenate(sl)).cuda(), kc, vc)
+        if plan.swapped_out:
+            ops.swap_blocks(spec, kc, vc, hk, hv, pairs_of(plan.swapped_out))
+            swapped += len(plan.swapped_out)
+        S = len(plan.decode_rids)
+        if S == 0:
+            continue
+        kv = [gen.trace_token_kv(cfg.seed, int(r), [int(q)], Hkv, D, dtype)
+              for r, q in zip(plan.decode_rids, plan.decode_pos)]
+        ops.append_tokens(spec, to_device(np.concatenate([a for a, _ in kv]), spec),
+                          to_device(np.concatenate([b for _, b in kv]), spec),
+                          torch.from_numpy(plan.decode_slots).cuda(), kc, vc,
+                          cow_pairs=torch.from_numpy(np.ascontiguousarray(plan.decode_cows)).cuda())
+        tables, ctx = sched.alloc.batch_metadata(plan.decode_rids, max_blocks)
+        q_host = np.stack([gen.trace_query(cfg.seed, int(r), int(q), Hq, D, dtype)
+                           for r, q in zip(plan.decode_rids, plan.decode_pos)])
+        out = torch.full((S, Hq, D), float("nan"), dtype=spec.torch_dtype, device="cuda")
+        ops.paged_attn_decode(spec, out, to_device(q_host, spec), kc, vc,
+                              torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(), scale,
+                              num_units=37)
+        got = to_float64(to_storage(out), dtype)
+        ref = []
+        for i, (r, q) in enumerate(zip(plan.decode_rids, plan.decode_pos)):
+            K, V = gen.trace_token_kv(cfg.seed, int(r), range(int(q) + 1), Hkv, D, dtype)
+            ref.append(contiguous_decode(q_host[i], K, V, scale, dtype))
+        assert_close(got, np.stack(ref), dtype, f"step {n}")
+        decoded += S
+    assert swapped > 0 and swapped_back > 0, (swapped, swapped_back)
+    assert decoded > 300

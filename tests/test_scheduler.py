@@ -147,3 +147,81 @@ def test_library_scheduler_equals_model_with_prefix_caching(name, num_blocks, st
     assert lib.alloc.prefix_stats() == (model.alloc.lookups, model.alloc.hits, len(model.alloc.cached))
     if num_blocks is not None:
         assert preempted > 0, "the small pool was meant to force preemption"
+
+
+# The same four-block trace with a two-block host pool (swap preemption), worked by
+# hand.  Steps 0-5 are unchanged.  Step 6: request 3's append finds no block; the
+# youngest request, 5 (one block), fits in the host pool and is swapped out (device
+# block 1 -> host block 0); request 4's append then finds no block either, and 4
+# itself (two blocks, one host block left) is preempted for recompute.  Step 7:
+# request 5 comes back first (host block 0 -> device block 2); 4 cannot be admitted.
+HAND_SWAP = HAND[:6] + [
+    ([],
+     dict(finished=[], admitted=[], preempted=[4], prefill=[], decode=[(3, 4, 4, None)],
+          swapped_out=[(5, [(1, 0)])], swapped_in=[])),
+    ([],
+     dict(finished=[], admitted=[], preempted=[], prefill=[],
+          decode=[(3, 5, 5, None), (5, 4, 0, None)], swapped_out=[], swapped_in=[(5, [(0, 2)])])),
+]
+
+
+def _swap_events(rec):
+    return dict(swapped_out=[(int(r), [tuple(int(x) for x in p) for p in ps]) for r, ps in rec.swapped_out],
+                swapped_in=[(int(r), [tuple(int(x) for x in p) for p in ps]) for r, ps in rec.swapped_in])
+
+
+def test_model_reproduces_hand_worked_swap_trace():
+    m = SchedulerModel(4, 4, 4, num_host_blocks=2)
+    for n, (arr, expect) in enumerate(HAND_SWAP):
+        got = _model_events(m.step(n, arr)) if "swapped_out" not in expect else None
+        if got is not None:
+            assert got == expect, f"step {n}"
+            continue
+        rec = m.step(n, arr)
+        exp = dict(expect)
+        swaps = {k: exp.pop(k) for k in ("swapped_out", "swapped_in")}
+        assert _model_events(rec) == exp, f"step {n}"
+        assert _swap_events(rec) == swaps, f"step {n}"
+    assert [r.rid for r in m.running] == [3, 5] and [r.rid for r in m.waiting] == [4]
+    assert m.alloc.free_list() == [] and list(m.alloc.host_free) == [1, 0]
+
+
+def test_library_reproduces_hand_worked_swap_trace():
+    s = TraceScheduler(4, 4, 4, num_host_blocks=2)
+    for n, (arr, expect) in enumerate(HAND_SWAP):
+        plan = s.step(n, arr)
+        exp = dict(expect)
+        swaps = {k: exp.pop(k) for k in ("swapped_out", "swapped_in") if k in exp}
+        assert _plan_events(plan) == exp, f"step {n}"
+        if swaps:
+            assert _swap_events(plan) == swaps, f"step {n}"
+    assert s.running_ids() == [3, 5] and s.waiting_ids() == [4]
+    assert s.alloc.free_list() == [] and s.alloc.host_free_list() == [1, 0]
+
+
+@pytest.mark.parametrize("name,num_blocks,host,steps", [("trace_13b", 3000, 600, 120),
+                                                        ("trace_13b", 3000, 40, 120),
+                                                        ("trace_prefix", 6000, 800, 120)])
+def test_library_scheduler_equals_model_with_swapping(name, num_blocks, host, steps):
+    """Pools small enough to preempt; a host pool large enough to swap most victims,
+    and one so small that most are recomputed."""
+    cfg = CONFIGS[name]
+    order = gen.pool_permutation(cfg.seed, num_blocks)
+    gt = cfg.gen_token if cfg.prefix else None
+    model = SchedulerModel(num_blocks, cfg.block_size, cfg.chunk, order, gen_token=gt,
+                           num_host_blocks=host)
+    lib = TraceScheduler(num_blocks, cfg.block_size, cfg.chunk, order, gen_token=gt,
+                         num_host_blocks=host)
+    swapped = recomputed = 0
+    for n in range(steps):
+        arr = cfg.arrivals(n)
+        rec = model.step(n, arr)
+        plan = lib.step(n, arr)
+        assert _plan_events(plan) == _model_events(rec), f"step {n}"
+        assert _swap_events(plan) == _swap_events(rec), f"step {n}"
+        swapped += len(rec.swapped_out)
+        recomputed += len(rec.preempted)
+        if n % 10 == 0:
+            assert lib.alloc.free_list() == model.alloc.free_list()
+            assert lib.alloc.host_free_list() == list(model.alloc.host_free)
+    assert swapped > 0
