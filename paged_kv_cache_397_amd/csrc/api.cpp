@@ -335,10 +335,10 @@ pa_status pa_paged_attn_prefill(const pa_cache_desc* d, void* out, const void* q
         return PA_ERR_INVALID_ARG;
     const int32_t tpb = d->block_size / pkv::kTile;
     // int32 in the kernel: cache tile indices, positions, and the workgroup count
-    // (at most num_seqs * Hkv * (max_query_len / 4 + 1) rounded up to 8)
+    // (at most (num_seqs * Hkv + 7) * (max_query_len / 8 + 1))
     if (static_cast<double>(d->num_blocks) * d->num_kv_heads * tpb >= 2147483647.0 ||
         static_cast<double>(max_blocks_per_seq) * d->block_size >= 2147483647.0 ||
-        static_cast<double>(num_seqs) * d->num_kv_heads * (max_query_len / 4.0 + 2) >=
+        (static_cast<double>(num_seqs) * d->num_kv_heads + 8) * (max_query_len / 8.0 + 2) >=
             2147483647.0)
         return PA_ERR_UNSUPPORTED;
     pkv::PrefillArgs a;

@@ -41,8 +41,9 @@
 //
 // Workgroups are renumbered so that every workgroup of one (sequence, KV head) runs
 // on the same XCD (workgroups are dealt to the eight XCDs round-robin and each XCD
-// has its own L2), and the query blocks with the most keys (the end of a chunk)
-// start first.
+// has its own L2), the (sequence, KV head) pairs are dealt to the XCDs round-robin
+// (an even mix of lengths per XCD), and the query blocks with the most keys (the end
+// of a chunk) start first.
 
 #include <type_traits>
 
@@ -58,6 +59,7 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kXcds = 8;
 constexpr int kPairKeys = 2 * kTile;
 constexpr float kMaxSlack = 8.f;           // base-2 headroom before m moves
+constexpr int kStages = 4;                 // LDS buffers: pairs p .. p + 3 resident or in flight
 
 typedef __bf16 bf16x2v __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
@@ -66,15 +68,26 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
+// IEEE maximum (NaN-propagating): gfx950 has it as one instruction that needs no
+// quieting of its inputs, unlike fmaxf.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Maximum over the four lanes 16 apart that hold one column (lanes i, i + 16, i + 32,
 // i + 48), with the gfx950 row-swap permutes.
 __device__ __forceinline__ float column_max(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Byte address of an LDS object, as the ds_* instructions take it.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+    return static_cast<uint32_t>(
+        reinterpret_cast<size_t>((const char __attribute__((address_space(3)))*)p));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -88,53 +101,79 @@ struct ColState {
     float m;            // the column's reference maximum (base 2)
 };
 
-// Fold one pair into one query block.  kEdge: some key of the pair is past the
-// block's first causal limit or past the sequence end (per-column masks, zeroed V
-// rows past vlim); otherwise every key is visible to every column.
-template <int D, bool kEdge>
-__device__ __forceinline__ void fold_pair(ColState<D>& st, const u32x4 (&q)[D / 32],
+// Fold one pair into the wave's NB query blocks together (their MFMA chains
+// interleave).  kEdge: some key of the pair may be past a column's causal limit or
+// past the sequence end: per-column masks, and V rows at or past vlim zeroed (they
+// may hold anything, and a zero weight times NaN is NaN).  Otherwise every key is
+// visible to every column.  c >= 0 (scale * log2 e).
+template <int D, int NB, bool kEdge>
+__device__ __forceinline__ void fold_pair(ColState<D> (&st)[NB], const u32x4 (&q)[NB][D / 32],
                                           const u32x4 (&k0)[D / 32], const u32x4 (&k1)[D / 32],
-                                          const u32x4 (&va)[D / 16], int key0, int lim, int vlim,
-                                          float c, int j) {
-    constexpr int NL = D / 32;
-    f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+                                          u32x4 (&va)[D / 16], int key0,
+                                          const int (&lim)[NB], int vlim, float c, int j) {
+    constexpr int NL = D / 32, NG = D / 16;
+    f32x4 S0[NB], S1[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) S0[b] = S1[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NL; ++s) {
-        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0[s]),
-                                                     __builtin_bit_cast(bf16x8, q[s]), S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1[s]),
-                                                     __builtin_bit_cast(bf16x8, q[s]), S1, 0, 0, 0);
-    }
-    // scores in base-2 units (scale * log2 e folded in)
-    float x[8] = {S0[0] * c, S0[1] * c, S0[2] * c, S0[3] * c,
-                  S1[0] * c, S1[1] * c, S1[2] * c, S1[3] * c};
-    if constexpr (kEdge) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int key = key0 + (r >> 2) * kTile + 4 * j + (r & 3);
-            x[r] = key < lim ? x[r] : kNegInf;
+        for (int b = 0; b < NB; ++b) {
+            S0[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0[s]),
+                                                            __builtin_bit_cast(bf16x8, q[b][s]),
+                                                            S0[b], 0, 0, 0);
+            S1[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1[s]),
+                                                            __builtin_bit_cast(bf16x8, q[b][s]),
+                                                            S1[b], 0, 0, 0);
         }
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mx = column_max(mx);
-    const bool move = mx > st.m + kMaxSlack;
-    if (__ballot(move)) {
-        const float mn = move ? mx : st.m;
-        const float alpha = fast_exp2(st.m - mn);
+    float x[NB][8], mx[NB];
+    bool any = false;
 #pragma unroll
-        for (int g = 0; g < D / 16; ++g) st.acc[g] *= alpha;
-        st.lsum *= alpha;
-        st.m = mn;
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            x[b][r] = S0[b][r];
+            x[b][4 + r] = S1[b][r];
+        }
+        if constexpr (kEdge) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int key = key0 + (r >> 2) * kTile + 4 * j + (r & 3);
+                x[b][r] = key < lim[b] ? x[b][r] : kNegInf;
+            }
+        }
+        float m8 = vmax(vmax(vmax(x[b][0], x[b][1]), vmax(x[b][2], x[b][3])),
+                        vmax(vmax(x[b][4], x[b][5]), vmax(x[b][6], x[b][7])));
+        mx[b] = column_max(m8) * c;
+        any |= mx[b] > st[b].m + kMaxSlack;
     }
-    uint32_t pw[4];
+    if (__ballot(any)) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        pw[r] = pack_bf16(fast_exp2(x[2 * r] - st.m), fast_exp2(x[2 * r + 1] - st.m));
-    const bf16x8 pB = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
+        for (int b = 0; b < NB; ++b) {
+            const float mn = mx[b] > st[b].m + kMaxSlack ? mx[b] : st[b].m;
+            const float alpha = fast_exp2(st[b].m - mn);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) st[b].acc[g] *= alpha;
+            st[b].lsum *= alpha;
+            st[b].m = mn;
+        }
+    }
+    bf16x8 pB[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        uint32_t pw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            pw[r] = pack_bf16(fast_exp2(__builtin_fmaf(x[b][2 * r], c, -st[b].m)),
+                              fast_exp2(__builtin_fmaf(x[b][2 * r + 1], c, -st[b].m)));
+        pB[b] = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
+    }
+    // the V operands were read by inline asm the compiler does not track: wait here
+#pragma unroll
+    for (int g = 0; g < NG; ++g) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(va[g]));
     uint32_t m00 = 0xffffffffu, m01 = 0xffffffffu, m10 = 0xffffffffu, m11 = 0xffffffffu;
     if constexpr (kEdge) {
-        // value rows at or past vlim may hold anything (a zero weight times NaN is NaN)
         const int nv0 = vlim - (key0 + 4 * j), nv1 = nv0 - kTile;
         m00 = (nv0 > 0 ? 0x0000ffffu : 0u) | (nv0 > 1 ? 0xffff0000u : 0u);
         m01 = (nv0 > 2 ? 0x0000ffffu : 0u) | (nv0 > 3 ? 0xffff0000u : 0u);
@@ -142,17 +181,21 @@ __device__ __forceinline__ void fold_pair(ColState<D>& st, const u32x4 (&q)[D / 
         m11 = (nv1 > 2 ? 0x0000ffffu : 0u) | (nv1 > 3 ? 0xffff0000u : 0u);
     }
 #pragma unroll
-    for (int g = 0; g < D / 16; ++g) {
+    for (int g = 0; g < NG; ++g) {
         bf16x8 vA;
         if constexpr (kEdge)
             vA = as_bf16x8(va[g][0] & m00, va[g][1] & m01, va[g][2] & m10, va[g][3] & m11);
         else
             vA = __builtin_bit_cast(bf16x8, va[g]);
-        st.acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pB, st.acc[g], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            st[b].acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pB[b], st[b].acc[g], 0, 0, 0);
     }
     const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
-    st.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(one2, one2, one2, one2), pB,
-                                                      st.lsum, 0, 0, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        st[b].lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(one2, one2, one2, one2),
+                                                             pB[b], st[b].lsum, 0, 0, 0);
 }
 
 template <int D, int G>
@@ -163,24 +206,24 @@ void prefill_kernel(PrefillArgs a) {
     constexpr int TB = 16 / G;                 // chunk tokens per query block
     constexpr int REGION = 2 * D;              // 16-B chunks in one K or V tile
     constexpr int PAIR = 4 * REGION;           // chunks in a pair: K t0, V t0, K t1, V t1
-    constexpr int LPT = PAIR / kThreads;       // chunks each thread carries per pair
-    // LDS buffer: K t0 | K t1 | V operands.  V operand (g, lane) is 16 bytes: the
-    // 8-byte half (g & 1) of V chunk (g / 2) * 64 + lane of tile 0, then the same of
-    // tile 1 -- the PV operand of dims 16 g .. for that lane, one read.
-    constexpr int VOFF = 2 * REGION;
+    constexpr int LPT = PAIR / kThreads;       // chunks each thread copies per pair
     static_assert(PAIR % kThreads == 0 && REGION % kWave == 0, "pair split");
-    __shared__ u32x4 lds[2][PAIR];
+    static_assert((kStages - 2) * LPT < 16, "vmcnt immediate");
+    __shared__ u32x4 lds[kStages][PAIR];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = uni(tid / kWave);
 
-    // workgroup b runs on XCD b % 8: give XCD x the logical groups x * per .. x * per + per - 1
-    const int per = (a.num_groups + kXcds - 1) / kXcds;
-    const int lg = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-    if (lg >= a.num_groups) return;
-    const int qg = a.qgroups - 1 - lg % a.qgroups;  // last query blocks first
-    const int sh = lg / a.qgroups;
+    // Workgroup b runs on XCD x = b % 8.  XCD x takes the (sequence, KV head) pairs
+    // sh = x, x + 8, x + 16, ..., all query groups of one pair in a row (they share
+    // its K/V in that XCD's L2), the last query groups (most keys) first.  Dealing the
+    // pairs round-robin gives every XCD a similar mix of sequence lengths.
+    const int xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+    const int nsh = a.num_seqs * a.num_kv_heads;
+    if (k >= ((nsh - xcd + kXcds - 1) / kXcds) * a.qgroups) return;
+    const int sh = xcd + kXcds * (k / a.qgroups);
+    const int qg = a.qgroups - 1 - k % a.qgroups;
     const int h = sh % a.num_kv_heads;
     const int s = sh / a.num_kv_heads;
 
@@ -213,7 +256,17 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int k = 0; k < NL; ++k) q[b][k] = *reinterpret_cast<const u32x4*>(qrow + 32 * k + 8 * j);
     }
-    const float cs = a.scale_log2e;
+    // The pair maximum is taken on raw scores and scaled after, which needs c >= 0: for
+    // a negative scale, negate q (exact in bf16) and use -c, the same products.
+    float cs = a.scale_log2e;
+    if (cs < 0.f) {
+        cs = -cs;
+#pragma unroll
+        for (int b = 0; b < kQB; ++b) {
+#pragma unroll
+            for (int k = 0; k < NL; ++k) q[b][k] ^= 0x80008000u;
+        }
+    }
     // Pairs below p_fast are visible to every column of the wave (all four blocks
     // non-empty); the workgroup folds pairs 0 .. np - 1.
     int p_fast = 1 << 30;
@@ -224,52 +277,56 @@ void prefill_kernel(PrefillArgs a) {
     const int np = (lim_wg + kPairKeys - 1) / kPairKeys;
     const int nt = (lim_wg + kTile - 1) / kTile;  // tiles holding a visible key
 
-    // Cache offsets of tiles, 64 at a time: lane k of a window holds tile base + k.
+    // Block ids of tiles, 64 at a time: lane k of a window holds the block of tile
+    // base + k.  Window 0 is read here; window w + 1 is copied by wave 0 into an LDS
+    // ring when window w comes into use, 32 pairs before it is needed, so its copy
+    // is covered by the pair loop's waits and barriers like the K/V copies.
     const int tpb = a.tiles_per_block;
     const int32_t* bt = a.block_tables + static_cast<size_t>(s) * a.max_blocks;
-    auto window = [&](int base) -> int {
+    __shared__ int win_lds[2][kWave];
+    auto win_src = [&](int base) -> const int32_t* {
         const int t = base + lane;
-        if (t >= nt) return 0;  // past the visible tiles: any valid tile, never weighted
-        int blk = bt[t / tpb];
+        return bt + (t < nt ? t / tpb : 0);  // past the visible tiles: any valid tile, never weighted
+    };
+    auto copy_window = [&](int base) {
+        if (wv == 0)
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)win_src(base),
+                (void __attribute__((address_space(3)))*)&win_lds[(base / kWave) & 1][0], 4, 0, 0);
+    };
+    auto tile_offset = [&](int blk, int t) -> int {
         blk = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
         return (blk * a.num_kv_heads + h) * tpb + t % tpb;
     };
     const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
     const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
-    int w_cur = window(0);
-    int w_next = 2 * np > kWave ? window(kWave) : 0;
-    u32x4 stg[LPT];
-    // Thread tid carries chunks r * 256 + tid of the pair; region (chunk / REGION) is
-    // K t0, V t0, K t1, V t1, the same for every lane of a wave.
-    auto gload = [&](int p) {
+    int w_cur = *win_src(0);
+    if (2 * np > kWave) copy_window(kWave);
+    // Thread tid copies chunks r * 256 + tid of the pair straight from the cache into
+    // LDS (global_load_lds: lane l of a wave lands 16 bytes at the wave's LDS base +
+    // 16 l); region (chunk / REGION) is K t0, V t0, K t1, V t1, the same for every
+    // lane of a wave.  The compiler does not order these copies against LDS reads:
+    // the pair loop waits for them explicitly (vmcnt) before its barrier.
+    auto issue = [&](int p) {
         const int t0 = 2 * p;
         if (t0 > 0 && (t0 & (kWave - 1)) == 0) {
-            w_cur = w_next;
-            if (t0 + kWave < 2 * np) w_next = window(t0 + kWave);
+            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                         : "=v"(w_cur) : "v"(lds_addr(&win_lds[(t0 / kWave) & 1][lane])));
+            if (t0 + kWave < 2 * np) copy_window(t0 + kWave);
         }
+        u32x4* stage = lds[p % kStages];
 #pragma unroll
         for (int r = 0; r < LPT; ++r) {
             const int ch = r * kThreads + tid;
             const int reg = uni(ch / REGION);
-            const int toff = __builtin_amdgcn_readlane(w_cur, (t0 + (reg >> 1)) & (kWave - 1));
+            const int t = t0 + (reg >> 1);
+            const int toff = tile_offset(__builtin_amdgcn_readlane(w_cur, t & (kWave - 1)), t);
             const u32x4* base = (reg & 1) ? vc : kc;
-            stg[r] = base[static_cast<size_t>(toff) * REGION + ch % REGION];
-        }
-    };
-    auto lwrite = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < LPT; ++r) {
-            const int ch = r * kThreads + tid;
-            const int reg = uni(ch / REGION);
-            const int o = ch % REGION;
-            if ((reg & 1) == 0) {
-                lds[buf][(reg >> 1) * REGION + o] = stg[r];
-            } else {
-                uint2* v2 = reinterpret_cast<uint2*>(&lds[buf][VOFF]);
-                const int q0 = (2 * (o / kWave)) * kWave + o % kWave;  // operand (2 mm, lane)
-                v2[2 * q0 + (reg >> 1)] = make_uint2(stg[r][0], stg[r][1]);
-                v2[2 * (q0 + kWave) + (reg >> 1)] = make_uint2(stg[r][2], stg[r][3]);
-            }
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(
+                    base + static_cast<size_t>(toff) * REGION + ch % REGION),
+                (void __attribute__((address_space(3)))*)(stage + r * kThreads + wv * kWave),
+                16, 0, 0);
         }
     };
 
@@ -282,40 +339,57 @@ void prefill_kernel(PrefillArgs a) {
         st[b].m = kNegInf;
     }
 
-    gload(0);
-    lwrite(0);
-    if (np > 1) gload(1);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // One pair: read its K and V from LDS, fold it into the wave's blocks, carry the
-    // next pair into the other buffer, barrier.
+    for (int i = 0; i < kStages - 1 && i < np; ++i) issue(i);
+
+    // One pair: wait for its copies (and, through the barrier, everyone's), start the
+    // copy of pair p + 3 into the buffer pair p - 1 used, read K and V from LDS and
+    // fold the pair into the wave's blocks.
     auto pair_step = [&](int p, auto edge) {
         constexpr bool kEdge = decltype(edge)::value;
-        const u32x4* sb = lds[p & 1];
+        if (p + kStages - 2 < np)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | ((kStages - 2) * LPT));  // vmcnt(later pairs' copies)
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        if (p + kStages - 1 < np) issue(p + kStages - 1);
+        // K of both tiles, then the PV operands, read by inline asm: the compiler would
+        // make every LDS read wait for all copies in flight (it cannot tell the
+        // buffers apart), which would drain the pipeline each pair.  The K reads are
+        // waited for just below, the V reads in fold_pair before the PV products (LDS
+        // reads complete in order).
+        // PV operand of dims 16 g = 32 mm + 16 e: the 8-byte half e of V chunk
+        // mm * 64 + lane of tile 0, then the same of tile 1, read into the operand's
+        // halves.
+        const uint32_t laddr = lds_addr(lds[p % kStages]) + lane * 16;
         u32x4 k0[NL], k1[NL], va[NG];
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
-            k0[k] = sb[k * kWave + lane];
-            k1[k] = sb[REGION + k * kWave + lane];
+            asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(k0[k]) : "v"(laddr), "i"(k * kWave * 16));
+            asm volatile("ds_read_b128 %0, %1 offset:%2"
+                         : "=v"(k1[k]) : "v"(laddr), "i"(2 * REGION * 16 + k * kWave * 16));
         }
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int g = 0; g < NG; ++g) va[g] = sb[VOFF + g * kWave + lane];
-        const int key0 = p * kPairKeys;
+        for (int mm = 0; mm < NL; ++mm) {
 #pragma unroll
-        for (int b = 0; b < kQB; ++b) {
-            if constexpr (kEdge) {
-                // near the diagonal or the sequence end: masks on every block
-                if (key0 < lim_hi[b])  // else no key of the pair is visible to the block
-                    fold_pair<D, true>(st[b], q[b], k0, k1, va, key0, lim[b], L, cs, j);
-            } else {
-                fold_pair<D, false>(st[b], q[b], k0, k1, va, key0, 0, 0, cs, j);
+            for (int e = 0; e < 2; ++e) {
+                u32x2 lo, hi;
+                asm volatile("ds_read_b64 %0, %1 offset:%2"
+                             : "=v"(lo) : "v"(laddr), "i"(REGION * 16 + mm * kWave * 16 + 8 * e));
+                asm volatile("ds_read_b64 %0, %1 offset:%2"
+                             : "=v"(hi) : "v"(laddr), "i"(3 * REGION * 16 + mm * kWave * 16 + 8 * e));
+                va[2 * mm + e] = (u32x4){lo.x, lo.y, hi.x, hi.y};
             }
         }
-        if (p + 1 < np) {
-            lwrite((p + 1) & 1);  // that buffer was last read in pair p - 1
-            if (p + 2 < np) gload(p + 2);
-        }
-        // LDS writes done, then the barrier; no fence, so the loads in flight stay in flight
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // 2 NG V reads were issued after the K reads: waiting until at most min(2 NG, 15)
+        // LDS reads are outstanding leaves every K read done.
+#pragma unroll
+        for (int k = 0; k < NL; ++k)
+            asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(k0[k]), "+v"(k1[k]) : "i"(2 * NG > 15 ? 15 : 2 * NG));
+        // Near the diagonal or the sequence end every block is masked; a block that
+        // sees no key of the pair adds exact zeros (its maximum is already finite:
+        // every column sees key 0 in pair 0).
+        fold_pair<D, kQB, kEdge>(st, q, k0, k1, va, p * kPairKeys, lim, L, cs, j);
     };
     const int pf = min(p_fast, np);
     int p = 0;
@@ -345,7 +419,8 @@ void prefill_kernel(PrefillArgs a) {
 template <int D>
 hipError_t launch_group_size(int group, PrefillArgs& a, hipStream_t st) {
     const dim3 block(kThreads);
-    const dim3 grid(((a.num_groups + kXcds - 1) / kXcds) * kXcds);
+    const int nsh = a.num_seqs * a.num_kv_heads;
+    const dim3 grid(kXcds * ((nsh + kXcds - 1) / kXcds) * a.qgroups);
     switch (group) {
         case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, block, 0, st, a); break;
         case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, block, 0, st, a); break;
