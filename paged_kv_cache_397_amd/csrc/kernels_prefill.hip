@@ -207,7 +207,8 @@ void prefill_kernel(PrefillArgs a) {
     constexpr int REGION = 2 * D;              // 16-B chunks in one K or V tile
     constexpr int PAIR = 4 * REGION;           // chunks in a pair: K t0, V t0, K t1, V t1
     constexpr int LPT = PAIR / kThreads;       // chunks each thread copies per pair
-    static_assert(PAIR % kThreads == 0 && REGION % kWave == 0, "pair split");
+    static_assert(PAIR % kThreads == 0 && REGION % kWave == 0 && kThreads % REGION == 0 &&
+                      (kStages & (kStages - 1)) == 0, "pair split");
     static_assert((kStages - 2) * LPT < 16, "vmcnt immediate");
     __shared__ u32x4 lds[kStages][PAIR];
 
@@ -294,13 +295,14 @@ void prefill_kernel(PrefillArgs a) {
                 (const void __attribute__((address_space(1)))*)win_src(base),
                 (void __attribute__((address_space(3)))*)&win_lds[(base / kWave) & 1][0], 4, 0, 0);
     };
-    auto tile_offset = [&](int blk, int t) -> int {
+    // lane's tile base + lane: block id -> the tile's index in the cache (once per window)
+    auto tile_offset = [&](int blk, int base) -> int {
         blk = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
-        return (blk * a.num_kv_heads + h) * tpb + t % tpb;
+        return (blk * a.num_kv_heads + h) * tpb + (base + lane) % tpb;
     };
     const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
     const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
-    int w_cur = *win_src(0);
+    int w_cur = tile_offset(*win_src(0), 0);
     if (2 * np > kWave) copy_window(kWave);
     // Thread tid copies chunks r * 256 + tid of the pair straight from the cache into
     // LDS (global_load_lds: lane l of a wave lands 16 bytes at the wave's LDS base +
@@ -310,23 +312,23 @@ void prefill_kernel(PrefillArgs a) {
     auto issue = [&](int p) {
         const int t0 = 2 * p;
         if (t0 > 0 && (t0 & (kWave - 1)) == 0) {
+            int raw;
             asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                         : "=v"(w_cur) : "v"(lds_addr(&win_lds[(t0 / kWave) & 1][lane])));
+                         : "=v"(raw) : "v"(lds_addr(&win_lds[(t0 / kWave) & 1][lane])));
+            w_cur = tile_offset(raw, t0);
             if (t0 + kWave < 2 * np) copy_window(t0 + kWave);
         }
-        u32x4* stage = lds[p % kStages];
+        u32x4* stage = lds[p & (kStages - 1)];
 #pragma unroll
         for (int r = 0; r < LPT; ++r) {
-            const int ch = r * kThreads + tid;
-            const int reg = uni(ch / REGION);
-            const int t = t0 + (reg >> 1);
-            const int toff = tile_offset(__builtin_amdgcn_readlane(w_cur, t & (kWave - 1)), t);
-            const u32x4* base = (reg & 1) ? vc : kc;
+            // this wave's 64 chunks of copy r: rw .. rw + 63, all in one region
+            const int rw = r * kThreads + wv * kWave;
+            const int reg = r * (kThreads / REGION) + (wv * kWave) / REGION;
+            const int toff = __builtin_amdgcn_readlane(w_cur, (t0 + (reg >> 1)) & (kWave - 1));
+            const u32x4* src = ((reg & 1) ? vc : kc) + static_cast<size_t>(toff) * REGION;
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(
-                    base + static_cast<size_t>(toff) * REGION + ch % REGION),
-                (void __attribute__((address_space(3)))*)(stage + r * kThreads + wv * kWave),
-                16, 0, 0);
+                (const void __attribute__((address_space(1)))*)(src + (rw & (REGION - 1)) + lane),
+                (void __attribute__((address_space(3)))*)(stage + rw), 16, 0, 0);
         }
     };
 
@@ -360,7 +362,7 @@ void prefill_kernel(PrefillArgs a) {
         // PV operand of dims 16 g = 32 mm + 16 e: the 8-byte half e of V chunk
         // mm * 64 + lane of tile 0, then the same of tile 1, read into the operand's
         // halves.
-        const uint32_t laddr = lds_addr(lds[p % kStages]) + lane * 16;
+        const uint32_t laddr = lds_addr(lds[p & (kStages - 1)]) + lane * 16;
         u32x4 k0[NL], k1[NL], va[NG];
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
