@@ -101,22 +101,16 @@ struct ColState {
     float m;            // the column's reference maximum (base 2)
 };
 
-// Fold one pair into the wave's NB query blocks together (their MFMA chains
-// interleave).  kEdge: some key of the pair may be past a column's causal limit or
-// past the sequence end: per-column masks, and V rows at or past vlim zeroed (they
-// may hold anything, and a zero weight times NaN is NaN).  Otherwise every key is
-// visible to every column.  c >= 0 (scale * log2 e).
-template <int D, int NB, bool kEdge>
-__device__ __forceinline__ void fold_pair(ColState<D> (&st)[NB], const u32x4 (&q)[NB][D / 32],
-                                          const u32x4 (&k0)[D / 32], const u32x4 (&k1)[D / 32],
-                                          u32x4 (&va)[D / 16], int key0,
-                                          const int (&lim)[NB], int vlim, float c, int j) {
-    constexpr int NL = D / 32, NG = D / 16;
-    f32x4 S0[NB], S1[NB];
+// Scores of one pair for the wave's NB query blocks (four independent MFMA chains
+// for NB = 2): S0 for tile 0, S1 for tile 1.
+template <int D, int NB>
+__device__ __forceinline__ void pair_scores(f32x4 (&S0)[NB], f32x4 (&S1)[NB],
+                                            const u32x4 (&q)[NB][D / 32],
+                                            const u32x4 (&k0)[D / 32], const u32x4 (&k1)[D / 32]) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) S0[b] = S1[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < NL; ++s) {
+    for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             S0[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0[s]),
@@ -127,7 +121,22 @@ __device__ __forceinline__ void fold_pair(ColState<D> (&st)[NB], const u32x4 (&q
                                                             S1[b], 0, 0, 0);
         }
     }
-    float x[NB][8], mx[NB];
+}
+
+// Folding one pair's scores into the wave's NB query blocks, in two steps so that
+// the next pair's score products can run between them: fold_max takes the scores to
+// base 2 units with masks, updates each column's reference maximum and rescales
+// the accumulators when it moves; fold_pv forms the weights and accumulates
+// O^T += V^T P^T and l += 1 P^T.  kEdge: some key of the pair may be past a column's
+// causal limit or past the sequence end: per-column masks, and V rows at or past
+// vlim zeroed (they may hold anything, and a zero weight times NaN is NaN).
+// Otherwise every key is visible to every column.  c >= 0 (scale * log2 e).
+template <int D, int NB, bool kEdge>
+__device__ __forceinline__ void fold_max(ColState<D> (&st)[NB], float (&x)[NB][8],
+                                         const f32x4 (&S0)[NB], const f32x4 (&S1)[NB], int key0,
+                                         const int (&lim)[NB], float c, int j) {
+    constexpr int NG = D / 16;
+    float mx[NB];
     bool any = false;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -159,6 +168,12 @@ __device__ __forceinline__ void fold_pair(ColState<D> (&st)[NB], const u32x4 (&q
             st[b].m = mn;
         }
     }
+}
+
+template <int D, int NB, bool kEdge>
+__device__ __forceinline__ void fold_pv(ColState<D> (&st)[NB], const float (&x)[NB][8],
+                                        u32x4 (&va)[D / 16], int key0, int vlim, float c, int j) {
+    constexpr int NG = D / 16;
     bf16x8 pB[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -343,34 +358,24 @@ void prefill_kernel(PrefillArgs a) {
 
     for (int i = 0; i < kStages - 1 && i < np; ++i) issue(i);
 
-    // One pair: wait for its copies (and, through the barrier, everyone's), start the
-    // copy of pair p + 3 into the buffer pair p - 1 used, read K and V from LDS and
-    // fold the pair into the wave's blocks.
-    auto pair_step = [&](int p, auto edge) {
-        constexpr bool kEdge = decltype(edge)::value;
-        if (p + kStages - 2 < np)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | ((kStages - 2) * LPT));  // vmcnt(later pairs' copies)
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
-        asm volatile("s_barrier" ::: "memory");
-        if (p + kStages - 1 < np) issue(p + kStages - 1);
-        // K of both tiles, then the PV operands, read by inline asm: the compiler would
-        // make every LDS read wait for all copies in flight (it cannot tell the
-        // buffers apart), which would drain the pipeline each pair.  The K reads are
-        // waited for just below, the V reads in fold_pair before the PV products (LDS
-        // reads complete in order).
-        // PV operand of dims 16 g = 32 mm + 16 e: the 8-byte half e of V chunk
-        // mm * 64 + lane of tile 0, then the same of tile 1, read into the operand's
-        // halves.
+    // LDS reads by inline asm: the compiler would make every LDS read wait for all
+    // copies in flight (it cannot tell the buffers apart), which would drain the
+    // pipeline each pair.  LDS reads complete in order; the waits below rely on it.
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    auto read_k = [&](int p, u32x4 (&k0)[NL], u32x4 (&k1)[NL]) {
         const uint32_t laddr = lds_addr(lds[p & (kStages - 1)]) + lane * 16;
-        u32x4 k0[NL], k1[NL], va[NG];
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
             asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(k0[k]) : "v"(laddr), "i"(k * kWave * 16));
             asm volatile("ds_read_b128 %0, %1 offset:%2"
                          : "=v"(k1[k]) : "v"(laddr), "i"(2 * REGION * 16 + k * kWave * 16));
         }
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    };
+    // PV operand of dims 16 g = 32 mm + 16 e: the 8-byte half e of V chunk mm * 64 + lane
+    // of tile 0, then the same of tile 1, read into the operand's halves (fold_pair
+    // waits for them).
+    auto read_v = [&](int p, u32x4 (&va)[NG]) {
+        const uint32_t laddr = lds_addr(lds[p & (kStages - 1)]) + lane * 16;
 #pragma unroll
         for (int mm = 0; mm < NL; ++mm) {
 #pragma unroll
@@ -383,20 +388,71 @@ void prefill_kernel(PrefillArgs a) {
                 va[2 * mm + e] = (u32x4){lo.x, lo.y, hi.x, hi.y};
             }
         }
-        // 2 NG V reads were issued after the K reads: waiting until at most min(2 NG, 15)
-        // LDS reads are outstanding leaves every K read done.
+    };
+
+    // Software pipeline: the loop step for pair p computes the scores of pair p + 1
+    // (matrix cores) while it folds pair p (softmax on the vector ALUs, then PV).
+    // Pair 0's scores first: wait for its copies (later pairs' may stay in flight).
+    f32x4 S0[kQB], S1[kQB];
+    if (np >= kStages - 1)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | ((kStages - 2) * LPT));
+    else
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("s_barrier" ::: "memory");
+    {
+        u32x4 k0[NL], k1[NL];
+        read_k(0, k0, k1);
 #pragma unroll
-        for (int k = 0; k < NL; ++k)
-            asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(k0[k]), "+v"(k1[k]) : "i"(2 * NG > 15 ? 15 : 2 * NG));
+        for (int k = 0; k < NL; ++k) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k0[k]), "+v"(k1[k]));
+        pair_scores<D, kQB>(S0, S1, q, k0, k1);
+    }
+
+    // Step p: wait for pair p + 1's copies and barrier (pair p - 1's buffer is then
+    // free: its K was read in step p - 2, its V in step p - 1), start the copy of pair
+    // p + 3 into it, read K of pair p + 1 and V of pair p, score pair p + 1, fold pair p.
+    auto pair_step = [&](int p, auto edge, auto next) {
+        constexpr bool kEdge = decltype(edge)::value;
+        constexpr bool kNext = decltype(next)::value;
+        if constexpr (kNext) {
+            if (p + kStages - 1 <= np)
+                __builtin_amdgcn_s_waitcnt(0x0F70 | ((kStages - 3) * LPT));  // pair p + 2's may stay
+            else
+                __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
+            asm volatile("s_barrier" ::: "memory");
+            if (p + kStages - 1 < np) issue(p + kStages - 1);
+        }
+        u32x4 k0[NL], k1[NL], va[NG];
+        f32x4 N0[kQB], N1[kQB];
+        if constexpr (kNext) read_k(p + 1, k0, k1);
+        read_v(p, va);
         // Near the diagonal or the sequence end every block is masked; a block that
         // sees no key of the pair adds exact zeros (its maximum is already finite:
         // every column sees key 0 in pair 0).
-        fold_pair<D, kQB, kEdge>(st, q, k0, k1, va, p * kPairKeys, lim, L, cs, j);
+        float x[kQB][8];
+        fold_max<D, kQB, kEdge>(st, x, S0, S1, p * kPairKeys, lim, cs, j);
+        if constexpr (kNext) {
+            // 2 NG V reads were issued after the K reads: at most min(2 NG, 15) LDS reads
+            // outstanding leaves every K read done
+#pragma unroll
+            for (int k = 0; k < NL; ++k)
+                asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(k0[k]), "+v"(k1[k]) : "i"(2 * NG > 15 ? 15 : 2 * NG));
+            pair_scores<D, kQB>(N0, N1, q, k0, k1);
+        }
+        fold_pv<D, kQB, kEdge>(st, x, va, p * kPairKeys, L, cs, j);
+        if constexpr (kNext) {
+#pragma unroll
+            for (int b = 0; b < kQB; ++b) {
+                S0[b] = N0[b];
+                S1[b] = N1[b];
+            }
+        }
     };
-    const int pf = min(p_fast, np);
+    // Pairs below p_fast are unmasked; the last pair is always masked (pf <= np - 1).
+    const int pf = min(p_fast, np - 1);
     int p = 0;
-    for (; p < pf; ++p) pair_step(p, std::false_type{});
-    for (; p < np; ++p) pair_step(p, std::true_type{});
+    for (; p < pf; ++p) pair_step(p, std::false_type{}, std::true_type{});
+    for (; p < np - 1; ++p) pair_step(p, std::true_type{}, std::true_type{});
+    pair_step(np - 1, std::true_type{}, std::false_type{});
 
 #pragma unroll
     for (int b = 0; b < kQB; ++b) {
