@@ -42,9 +42,10 @@
 // Workgroups are renumbered so that every workgroup of one (sequence, KV head) runs
 // on the same XCD (workgroups are dealt to the eight XCDs round-robin and each XCD
 // has its own L2), the (sequence, KV head) pairs are dealt to the XCDs round-robin
-// (an even mix of lengths per XCD), and the query blocks with the most keys (the end
-// of a chunk) start first.
+// (an even mix of lengths per XCD), the longest sequences start first, and within a
+// sequence the query blocks with the most keys (the end of a chunk) start first.
 
+#include <climits>
 #include <type_traits>
 
 #include "kernels_common.h"
@@ -236,12 +237,41 @@ void prefill_kernel(PrefillArgs a) {
     // its K/V in that XCD's L2), the last query groups (most keys) first.  Dealing the
     // pairs round-robin gives every XCD a similar mix of sequence lengths.
     const int xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
-    const int nsh = a.num_seqs * a.num_kv_heads;
+    const int Hkv = a.num_kv_heads;
+    const int nsh = a.num_seqs * Hkv;
     if (k >= ((nsh - xcd + kXcds - 1) / kXcds) * a.qgroups) return;
-    const int sh = xcd + kXcds * (k / a.qgroups);
     const int qg = a.qgroups - 1 - k % a.qgroups;
-    const int h = sh % a.num_kv_heads;
-    const int s = sh / a.num_kv_heads;
+    int jj = k / a.qgroups;  // this workgroup's (sequence, KV head) among the XCD's
+    int s, h;
+    if (a.num_seqs <= kWave) {
+        // Longest sequences first (ties: lower index), so that the longest workgroups
+        // do not start last: rank the cache lengths across the lanes, then walk the
+        // ranks.  Sequence s has the heads h = (x - s Hkv) mod 8, + 8, ... on XCD x.
+        const int lane0 = threadIdx.x & (kWave - 1);
+        const int Ls = lane0 < a.num_seqs ? a.context_lens[lane0] : INT_MIN;
+        int rank = 0;
+        for (int t = 0; t < a.num_seqs; ++t) {
+            const int Lt = __builtin_amdgcn_readlane(Ls, t);
+            rank += (Lt > Ls) || (Lt == Ls && t < lane0);
+        }
+        s = 0;
+        h = 0;
+        for (int r = 0; r < a.num_seqs; ++r) {
+            const int sr = __builtin_ffsll(__ballot(rank == r && lane0 < a.num_seqs)) - 1;
+            const int h0 = (((xcd - sr * Hkv) % kXcds) + kXcds) % kXcds;
+            const int cnt = h0 < Hkv ? (Hkv - 1 - h0) / kXcds + 1 : 0;
+            if (jj < cnt) {
+                s = sr;
+                h = h0 + kXcds * jj;
+                break;
+            }
+            jj -= cnt;
+        }
+    } else {
+        const int sh = xcd + kXcds * jj;
+        h = sh % Hkv;
+        s = sh / Hkv;
+    }
 
     const int r0 = a.query_start[s], r1 = a.query_start[s + 1];
     const int c = r1 - r0;
