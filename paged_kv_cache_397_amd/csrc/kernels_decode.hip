@@ -36,6 +36,84 @@
 namespace pkv {
 namespace {
 
+// ---------------------------------------------------------------------------------
+// One 16-token tile folded into a group accumulator with the matrix cores.
+//
+// Sixteen columns share the K/V tile of one KV head: the G query heads of that
+// head, repeated with period G.  Lane l = 16 j + i owns column i.
+//   S^T = K Q^T: v_mfma_f32_16x16x32_bf16, one per 32 dims; A = the K tile as
+//     loaded (token i, dims 32 s + 8 j ..), B = the column's query (same dims).
+//     Lane (j, i) gets the scores of tokens 4 j .. 4 j + 3 for column i.
+//   Online softmax per column in base 2 (scores times scale * log2 e); P is
+//     rounded to bf16 in the accumulator layout, which is the B operand of
+//   O^T = V^T P^T: v_mfma_f32_16x16x16_bf16, one per 16 dims, fp32 accumulate.
+//     acc[g][r] is dim 16 g + 4 j + r of column i.
+// Token k of tile t is visible when 16 t + k < lim.  Value rows of tokens at or past
+// vlim (the sequence length) are zeroed first: their slots may hold anything, and
+// a zero weight times a NaN would still poison the sum; vlim must be uniform over
+// the wave.  Every column must see at least one token of the first tile it folds, so
+// that its running max is finite.
+template <int D>
+struct GroupAcc {
+    float m, l;
+    f32x4 acc[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void group_tile(GroupAcc<D>& st, const u32x4 (&q)[D / 32],
+                                           const u32x4* kb, const u32x4* vb, int t, int lim,
+                                           int vlim, float scale_log2e, int lane) {
+    constexpr int NL = D / 32, NG = D / 16;
+    const int j = lane >> 4;
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NL; ++s)
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[s]),
+                                                    __builtin_bit_cast(bf16x8, q[s]), S, 0, 0, 0);
+    const int tok0 = t * kTile + 4 * j;
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < lim) ? S[r] * scale_log2e : kNegInf;
+    float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(st.m, tmax);
+    const float alpha = fast_exp2(st.m - m_new);
+    uint32_t pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        pb[r] = bf16_rne_finite(fast_exp2(sc[r] - m_new));
+        psum += __uint_as_float(pb[r] << 16);
+    }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    const s16x4 pB = __builtin_bit_cast(
+        s16x4, (unsigned __attribute__((ext_vector_type(2)))){pb[0] | (pb[1] << 16),
+                                                              pb[2] | (pb[3] << 16)});
+#pragma unroll
+    for (int g = 0; g < NG; ++g) st.acc[g] *= alpha;
+    const bool last = t * kTile + kTile > vlim;
+    uint32_t mask01 = 0xffffffffu, mask23 = 0xffffffffu;
+    if (last) {
+        const int nv = vlim - tok0;
+        mask01 = (nv > 0 ? 0x0000ffffu : 0u) | (nv > 1 ? 0xffff0000u : 0u);
+        mask23 = (nv > 2 ? 0x0000ffffu : 0u) | (nv > 3 ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int mm = 0; mm < NL; ++mm) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const unsigned w0 = vb[mm][2 * e] & mask01;
+            const unsigned w1 = vb[mm][2 * e + 1] & mask23;
+            const s16x4 vA = __builtin_bit_cast(
+                s16x4, (unsigned __attribute__((ext_vector_type(2)))){w0, w1});
+            st.acc[2 * mm + e] =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pB, st.acc[2 * mm + e], 0, 0, 0);
+        }
+    }
+}
+
 // Context length of sequence i, clamped to what its table row can address.
 __device__ __forceinline__ int ctx_of(const DecodeArgs& a, int i) {
     const int cap = a.max_blocks * a.tiles_per_block * kTile;
@@ -255,7 +333,7 @@ struct GroupPath {
     static __device__ __forceinline__ void tile(const DecodeArgs& a, Acc& st, const Q& q,
                                                 const u32x4* kb, const u32x4* vb, int t, int ctx,
                                                 int lane) {
-        group_tile<D, false>(st, q.v, kb, vb, t, ctx, ctx, a.scale_log2e, lane);
+        group_tile<D>(st, q.v, kb, vb, t, ctx, ctx, a.scale_log2e, lane);
     }
 
     static __device__ __forceinline__ void finish(const DecodeArgs& a, Acc& st, int row, int seq,

@@ -158,3 +158,21 @@ def test_serving_sized_chunks_sampled(Hq, Hkv):
         rows = sorted(set(rng.integers(0, int(b.c[s]), 46).tolist()) | {0, int(b.c[s]) - 1})
         got = out[[int(b.qs[s]) + r for r in rows]]
         assert_close(got, b.expected(s, rows=rows), "bf16", f"seq {s} L {b.L[s]} c {b.c[s]}")
+
+
+@pytest.mark.parametrize("S", [64, 70])
+def test_many_sequences_every_row(S):
+    """Batches at and past 64 sequences (the kernel ranks up to 64 sequences by length
+    to start the longest first, and keeps the given order beyond that): ragged
+    chunks of 1..40 tokens at the end of caches of 1..300 tokens, GQA 16/4, every
+    row against the oracle."""
+    spec = ops.CacheSpec(num_blocks=2048, block_size=16, num_kv_heads=4, head_dim=128,
+                         dtype="bf16")
+    rng = gen.stream(47, S)
+    L = rng.integers(1, 301, S)
+    specs = [(int(l), int(rng.integers(1, min(int(l), 40) + 1))) for l in L]
+    b = Chunks(spec, specs, 16, seed=47, free_order=gen.pool_permutation(47, 2048))
+    out = to_f64(b.run(), "bf16")
+    for s in range(b.S):
+        rows = slice(int(b.qs[s]), int(b.qs[s + 1]))
+        assert_close(out[rows], b.expected(s), "bf16", f"S {S} seq {s} L {b.L[s]} c {b.c[s]}")
