@@ -253,6 +253,9 @@ pa_status pa_paged_attn_decode_merge(const pa_cache_desc* desc, void* out, const
  * Supported: bf16 with G in {1, 2, 4, 8, 16} and D in {64, 128}
  * (PA_ERR_UNSUPPORTED otherwise).  Accumulation is fp32, P is rounded to bf16
  * before the PV product, and outputs are rounded nearest-even.  No workspace.
+ * A row's bits do not depend on how its prompt is cut into chunks, nor on the
+ * other rows or sequences of the call; a NaN in a visible key, value or query
+ * propagates to the row.
  */
 pa_status pa_paged_attn_prefill(const pa_cache_desc* desc, void* out, const void* q,
                                 const void* k_cache, const void* v_cache,
