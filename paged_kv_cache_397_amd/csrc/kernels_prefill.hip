@@ -242,43 +242,48 @@ void prefill_kernel(PrefillArgs a) {
     if (k >= ((nsh - xcd + kXcds - 1) / kXcds) * a.qgroups) return;
     const int qg = a.qgroups - 1 - k % a.qgroups;
     int jj = k / a.qgroups;  // this workgroup's (sequence, KV head) among the XCD's
-    int s, h;
+    int s, h, r0, r1, Lraw;
     if (a.num_seqs <= kWave) {
         // Longest sequences first (ties: lower index), so that the longest workgroups
-        // do not start last: rank the cache lengths across the lanes, then walk the
-        // ranks.  Sequence s has the heads h = (x - s Hkv) mod 8, + 8, ... on XCD x.
+        // do not start last.  Lane t ranks sequence t by cache length; a forward
+        // permute gives lane r the sequence of rank r; lane r counts that sequence's
+        // heads on this XCD (sequence s has heads h = (x - s Hkv) mod 8, + 8, ...);
+        // a scan over the lanes finds the rank whose heads hold entry jj.
         const int lane0 = threadIdx.x & (kWave - 1);
-        const int Ls = lane0 < a.num_seqs ? a.context_lens[lane0] : INT_MIN;
-        int rank = 0;
+        const bool is_seq = lane0 < a.num_seqs;
+        const int Ls = is_seq ? a.context_lens[lane0] : INT_MIN;
+        const int qa = is_seq ? a.query_start[lane0] : 0;
+        const int qb = is_seq ? a.query_start[lane0 + 1] : 0;
+        int rank = is_seq ? 0 : lane0;  // lanes past the batch keep distinct ranks >= S
         for (int t = 0; t < a.num_seqs; ++t) {
             const int Lt = __builtin_amdgcn_readlane(Ls, t);
-            rank += (Lt > Ls) || (Lt == Ls && t < lane0);
+            rank += is_seq && ((Lt > Ls) || (Lt == Ls && t < lane0));
         }
-        s = 0;
-        h = 0;
-        for (int r = 0; r < a.num_seqs; ++r) {
-            const int sr = __builtin_ffsll(__ballot(rank == r && lane0 < a.num_seqs)) - 1;
-            const int h0 = (((xcd - sr * Hkv) % kXcds) + kXcds) % kXcds;
-            const int cnt = h0 < Hkv ? (Hkv - 1 - h0) / kXcds + 1 : 0;
-            if (jj < cnt) {
-                s = sr;
-                h = h0 + kXcds * jj;
-                break;
-            }
-            jj -= cnt;
-        }
+        const int sr = __builtin_amdgcn_ds_permute(rank * 4, lane0);  // sequence of rank lane0
+        const int h0 = (xcd - sr * Hkv) & (kXcds - 1);
+        const int cnt = is_seq && h0 < Hkv ? (Hkv - 1 - h0) / kXcds + 1 : 0;
+        const int incl = wave_inclusive_scan(cnt, lane0);
+        const int r = uni(__builtin_ffsll(__ballot(incl > jj)) - 1);  // exists: jj < heads on XCD
+        s = __builtin_amdgcn_readlane(sr, r);
+        h = __builtin_amdgcn_readlane(h0, r) +
+            kXcds * (jj - (__builtin_amdgcn_readlane(incl, r) - __builtin_amdgcn_readlane(cnt, r)));
+        r0 = __builtin_amdgcn_readlane(qa, s);
+        r1 = __builtin_amdgcn_readlane(qb, s);
+        Lraw = __builtin_amdgcn_readlane(Ls, s);
     } else {
         const int sh = xcd + kXcds * jj;
         h = sh % Hkv;
         s = sh / Hkv;
+        r0 = a.query_start[s];
+        r1 = a.query_start[s + 1];
+        Lraw = a.context_lens[s];
     }
 
-    const int r0 = a.query_start[s], r1 = a.query_start[s + 1];
     const int c = r1 - r0;
     const int qb0 = qg * (kWaves * kQB);       // the workgroup's first query block
     if (r0 < 0 || r1 > a.num_tokens || c <= 0 || qb0 * TB >= c) return;  // uniform
     const int cap = a.max_blocks * a.tiles_per_block * kTile;
-    const int L = min(max(a.context_lens[s], 0), cap);
+    const int L = min(max(Lraw, 0), cap);
     const int start = L - c;  // position of the chunk's first token (>= 0 for valid input)
 
     const int j = lane >> 4, i = lane & 15;

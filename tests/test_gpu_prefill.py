@@ -176,3 +176,25 @@ def test_many_sequences_every_row(S):
     for s in range(b.S):
         rows = slice(int(b.qs[s]), int(b.qs[s + 1]))
         assert_close(out[rows], b.expected(s), "bf16", f"S {S} seq {s} L {b.L[s]} c {b.c[s]}")
+
+
+def test_rows_do_not_depend_on_the_rest_of_the_batch():
+    """Each sequence's rows are bit-identical whether it is prefilled alone or in a
+    ragged batch (different dispatch order, neighbours in the same workgroups)."""
+    spec = ops.CacheSpec(num_blocks=640, block_size=16, num_kv_heads=8, head_dim=128, dtype="bf16")
+    b = Chunks(spec, RAGGED, 32, seed=48, free_order=gen.pool_permutation(48, 640))
+    together = b.run()
+    for s in range(b.S):
+        c = int(b.c[s])
+        if c == 0:
+            continue
+        r0 = int(b.qs[s])
+        out = torch.full((c, 32, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ops.paged_attn_prefill(spec, out, b.q[r0:r0 + c].contiguous(), b.cache.k, b.cache.v,
+                               b.tables[s:s + 1].contiguous(),
+                               torch.tensor([0, c], dtype=torch.int32, device="cuda"),
+                               torch.tensor([int(b.L[s])], dtype=torch.int32, device="cuda"),
+                               1 / math.sqrt(128))
+        torch.cuda.synchronize()
+        alone = to_storage(out)
+        assert np.array_equal(alone.view(np.uint16), together[r0:r0 + c].view(np.uint16)), s
