@@ -138,6 +138,21 @@ def cpu_baseline(cfg, ctx, q_host, seconds):
         times.append(time.perf_counter() - t0)
     kv_bytes = int(sctx.sum()) * cfg.kv_bytes_per_token()
     t = float(np.median(times))
+    # the same sample on one thread (BLAS limited to one), a shorter budget
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1s = []
+            t_end = time.perf_counter() + seconds / 2
+            while not t1s or time.perf_counter() < t_end:
+                t0 = time.perf_counter()
+                paged_decode(lay, q, kc, vc, tables, sctx, cfg.scale)
+                t1s.append(time.perf_counter() - t0)
+        single = {"value": kv_bytes / float(np.median(t1s)) / 1e9, "unit": "GB/s", "cores": 1,
+                  "runs": len(t1s), "seconds_per_run": float(np.median(t1s))}
+    except Exception as exc:  # pragma: no cover
+        single = {"error": repr(exc)}
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -150,7 +165,8 @@ def cpu_baseline(cfg, ctx, q_host, seconds):
             "sample": (f"fp64 NumPy oracle (gather + textbook softmax) on every 4th sequence of "
                        f"the batch ({len(sample)} seqs, {int(sctx.sum())} tokens, "
                        f"{kv_bytes / 1e9:.3f} GB of KV), median of {len(times)} runs"),
-            "seconds_per_run": t, "cpu_model": cpu, "affinity_cpus": len(os.sched_getaffinity(0))}
+            "seconds_per_run": t, "cpu_model": cpu, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "single_thread": single}
 
 
 def run_trace(args):
@@ -835,6 +851,22 @@ def main():
         step(n, "profile")
     torch.cuda.synchronize()
     gc.enable()
+    # Cold pass 1: the last step's pass 1 run again (it reads the cache and writes
+    # only its outputs, so nothing changes) right after writing a 1 GiB buffer, more
+    # than the 256 MB MALL and every XCD's L2, so that its K/V come from HBM.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    _, last_partial, _ = calls[total_steps - 1]
+    cold = []
+    for _ in range(5):
+        flush.fill_(1.0)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        last_partial()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1) * 1e-3)
+    del flush
+    cold_bytes = float(ctx_now.sum()) * kv_per_tok
 
     tok = np.array([e[4] for e in ev["timed"]], dtype=np.float64)
     kv_bytes = tok * kv_per_tok
@@ -873,6 +905,17 @@ def main():
             "pass2_us_median": round(float(np.median(t_attn - t_pp1)) * 1e6, 2),
             "attn_gbps_median": round(float(np.median(pbytes / t_attn) / 1e9), 2),
         },
+        "cold_pass1": {
+            "note": "the last step's pass 1 after writing a 1 GiB buffer (MALL and L2 flushed), 5 runs",
+            "us_median": round(float(np.median(cold)) * 1e6, 2),
+            "gbps_median": round(cold_bytes / float(np.median(cold)) / 1e9, 2),
+        },
+        # useful matrix-core work of the grouped-query product (G > 1 runs on MFMA):
+        # 4 Hq D flops per cached token, over pass 1's median time
+        "mfma": ({"useful_tflops": round(4.0 * Hq * D * float(np.median(tok)) / float(np.median(t_p1)) / 1e12, 2),
+                  "frac_of_bf16_peak": round(4.0 * Hq * D * float(np.median(tok)) / float(np.median(t_p1))
+                                             / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                 if Hq > Hkv and cfg.dtype == "bf16" else None),
         "host_bookkeeping_us_median": round(float(np.median([h[0] for h in host])) * 1e6, 2),
         "host_step_us_median": round(float(np.median([h[1] for h in host])) * 1e6, 2),
         "host_step_us_max": round(float(np.max([h[1] for h in host])) * 1e6, 2),
