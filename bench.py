@@ -878,6 +878,22 @@ def main():
     t_attn = np.array([e[1].elapsed_time(e[3]) for e in pe]) * 1e-3
     value = float(kv_bytes.sum() / wall / 1e9)
     p1_gbps = float(np.median(kv_bytes / t_p1) / 1e9)
+    unique = None
+    if cfg.ctx_kind == "shared_prefix":
+        # Shared blocks are read by many sequences in one pass; count each physical
+        # block once with the tokens it holds (the tables before the first step), plus
+        # one private token per sequence for every step since (warm-up included).
+        held = {}
+        for i in range(S):
+            L = int(ctx0[i])
+            for kk in range(-(-L // B)):
+                blk = int(tables_h[i, kk])
+                held[blk] = max(held.get(blk, 0), min(B, L - kk * B))
+        first = float(sum(held.values()))
+        u_tok = first + S * (warm + 1 + np.arange(steps, dtype=np.float64))
+        unique = {"note": "each physical block counted once, private appends added per step",
+                  "unique_kv_bytes_first_timed_step": int(u_tok[0] * kv_per_tok),
+                  "unique_gbps": round(float((u_tok * kv_per_tok).sum() / wall / 1e9), 2)}
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -895,6 +911,7 @@ def main():
                    "kv_heads": Hkv, "head_dim": D, "block_size": B, "pool_blocks": cfg.num_blocks,
                    "sum_ctx_first_step": int(tok[0]), "units": units, "seed": cfg.seed},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "shared_prefix_unique": unique,
         "us_per_step": round(wall / steps * 1e6, 2),
         "breakdown": {
             "note": f"{len(pe)} untimed steps after the timed region, events around every launch",
