@@ -2,6 +2,9 @@
 reserved slots over the serving trace equal to the oracle's count at every step,
 for block sizes 8, 16, 32 and 64."""
 
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -19,6 +22,19 @@ def test_closed_forms():
     assert fixed_reserved(3, 4096) == 12288
     # a 2048-token request in a 4096 reservation: half wasted, the pages' ~50%
     assert utilisation(2048, fixed_reserved(1, 4096)) == 0.5
+
+
+def test_pages_worked_example():
+    """The hihuo.com page's example (tests/golden/allocator_examples.json): a 4096-slot
+    reservation for a request that uses 500 wastes about 88%; with 16-token pages
+    500 and 1000 tokens hold 32 and 63 pages."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "allocator_examples.json")))
+    w = g["preallocation_waste"]
+    waste = 1 - utilisation(w["used"], fixed_reserved(1, w["reserved"]))
+    assert round(100 * waste) == w["waste_percent_rounded"]
+    p = g["pages_for_tokens"]
+    for n, blocks in p["cases"]:
+        assert paged_reserved([n], p["block_size"]) == blocks * p["block_size"]
 
 
 @pytest.mark.parametrize("B", [8, 16, 32, 64])
