@@ -14,14 +14,14 @@
 //
 // Work split.  For one KV head, the G query heads of the chunk's tokens form
 // (token, head) columns, 16 to a query block: 16 / G consecutive tokens times the G
-// heads.  A workgroup of four waves owns 16 consecutive query blocks of one
-// (sequence, KV head); wave w folds blocks w, w + 4, w + 8 and w + 12, so that the
-// four waves reach the diagonal together.  Keys go by pairs of 16-token tiles: the
-// workgroup copies a pair's K and V (16 KiB at D = 128) from the paged cache into
-// LDS once, and every wave reads it from there for its 64 columns, so one byte
-// fetched from L2 feeds 256 columns.  Two LDS buffers alternate: while the waves
-// fold pair p, the registers of every thread carry pair p + 1 in from L2, and one
-// barrier per pair hands the buffers over.
+// heads.  A workgroup of four waves owns 8 consecutive query blocks of one
+// (sequence, KV head); wave w folds blocks w and w + 4, so that the four waves reach
+// the diagonal together.  Keys go by pairs of 16-token tiles: the workgroup copies
+// a pair's K and V (16 KiB at D = 128) straight from the paged cache into LDS once
+// (global_load_lds), and every wave reads it from there for its 32 columns, so one
+// byte fetched from L2 feeds 128 columns.  Four LDS buffers hold pairs p .. p + 3:
+// the copies run three pairs ahead, one barrier per pair hands a buffer over, and
+// the matrix cores compute the scores of pair p + 1 while pair p is folded.
 //
 // Tile math per (query block, pair), all on the matrix cores except the softmax:
 //   S^T = K Q^T    v_mfma_f32_16x16x32_bf16, 4 per tile (D = 128): lane (j, i)
@@ -233,9 +233,9 @@ void prefill_kernel(PrefillArgs a) {
     const int wv = uni(tid / kWave);
 
     // Workgroup b runs on XCD x = b % 8.  XCD x takes the (sequence, KV head) pairs
-    // sh = x, x + 8, x + 16, ..., all query groups of one pair in a row (they share
-    // its K/V in that XCD's L2), the last query groups (most keys) first.  Dealing the
-    // pairs round-robin gives every XCD a similar mix of sequence lengths.
+    // sh = s Hkv + h with sh = x (mod 8), all query groups of one pair in a row (they
+    // share its K/V in that XCD's L2), the last query groups (most keys) first.
+    // Dealing the pairs round-robin gives every XCD a similar mix of sequence lengths.
     const int xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
     const int Hkv = a.num_kv_heads;
     const int nsh = a.num_seqs * Hkv;
@@ -318,7 +318,7 @@ void prefill_kernel(PrefillArgs a) {
             for (int k = 0; k < NL; ++k) q[b][k] ^= 0x80008000u;
         }
     }
-    // Pairs below p_fast are visible to every column of the wave (all four blocks
+    // Pairs below p_fast are visible to every column of the wave (both blocks
     // non-empty); the workgroup folds pairs 0 .. np - 1.
     int p_fast = 1 << 30;
 #pragma unroll
@@ -407,7 +407,7 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
     // PV operand of dims 16 g = 32 mm + 16 e: the 8-byte half e of V chunk mm * 64 + lane
-    // of tile 0, then the same of tile 1, read into the operand's halves (fold_pair
+    // of tile 0, then the same of tile 1, read into the operand's halves (fold_pv
     // waits for them).
     auto read_v = [&](int p, u32x4 (&va)[NG]) {
         const uint32_t laddr = lds_addr(lds[p & (kStages - 1)]) + lane * 16;
