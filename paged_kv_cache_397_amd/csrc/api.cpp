@@ -190,9 +190,11 @@ int32_t pa_decode_default_units(void) {
         (void)hipGetLastError();
         cus = 256;
     }
-    // Five one-wave units per CU keep about 10 MiB of K/V reads in flight at one
-    // tile per wave, the measured optimum of pass 1 on MI355X (256 CUs -> 1280).
-    u = cus * 5;
+    // Eight one-wave units per CU: with eight KV heads (or query heads) per row
+    // group this is one eight-wave workgroup per CU, 16 MiB of K/V reads in flight
+    // at one tile per wave; the measured optimum of pass 1 on MI355X (256 CUs ->
+    // 2048).
+    u = cus * 8;
     g_default_units.store(u);
     return u;
 }
@@ -267,6 +269,13 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     a.tiles_per_block = tpb;
     a.num_blocks = d->num_blocks;
     a.num_units = units;
+    // Aligned split: with at least one unit per row, every row is cut into the same
+    // ranges, and the rows of a range (up to 8, a power of two dividing the row
+    // count) share a workgroup.
+    a.aligned = units >= rows ? 1 : 0;
+    a.waves_per_group = 1;
+    if (a.aligned)
+        while (a.waves_per_group < 8 && rows % (2 * a.waves_per_group) == 0) a.waves_per_group *= 2;
     a.scale_log2e = scale * 1.4426950408889634f;
     return from_hip(pkv::launch_decode(d->dtype, d->head_dim, use_group, a, passes,
                                        static_cast<hipStream_t>(stream)));

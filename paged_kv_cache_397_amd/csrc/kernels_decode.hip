@@ -11,12 +11,18 @@
 //
 // Work split ("units"): per work row (a KV head for the group kernel, a query
 // head for the per-head kernel) the sequences' 16-token tiles are laid end to
-// end, rows one after another, and the whole line is cut into num_units equal
-// ranges.  One wavefront owns one range: perfectly even work whatever the
-// length mix.  A sequence that a range holds whole is finished in place; a
-// sequence cut by range ends leaves partial (max, sum, accumulator) records,
-// and pass 2 merges them with the log-sum-exp rule.  Every wave scans the
-// context lengths itself to find its range, so no planning kernel runs first.
+// end.  With at least one unit per row, every row is cut into the same
+// num_units / rows ranges of C tiles (the aligned split), so the units of one
+// range cover the same tiles in every row; with fewer units than rows, the rows
+// are laid one after another and the whole line is cut into num_units equal
+// ranges.  One wavefront owns one range: even work whatever the length mix.
+// Under the aligned split, the rows of one range (up to eight) run as the waves
+// of one workgroup and meet once per tile, so the adjacent 4 KiB head slices of
+// a block are requested together.  A sequence that a range holds whole is
+// finished in place; a sequence cut by range ends leaves partial (max, sum,
+// accumulator) records, and pass 2 merges them with the log-sum-exp rule.
+// Every wave scans the context lengths itself to find its range, so no
+// planning kernel runs first.
 //
 // Two pass-1 kernels:
 //  * per-head (VALU): one query head per row.  A lane owns one token of the
@@ -557,34 +563,64 @@ __device__ __forceinline__ Chunk build_chunk(const DecodeArgs& a, Cursor c, int 
 }
 
 // ---------------------------------------------------------------------------------
-// Pass 1: one wavefront per unit.  The loop keeps the next tile's K/V loads
-// (and, when that tile opens a new piece, the new query) in flight while the
-// current tile is folded in.
-template <class Path, typename T, int D>
-__global__ __launch_bounds__(64) void decode_pass1(DecodeArgs a) {
+// Pass 1: one wavefront per unit, NW units (rows of one range) per workgroup.
+// The loop keeps the next tile's K/V loads (and, when that tile opens a new
+// piece, the new query) in flight while the current tile is folded in.
+template <class Path, typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     constexpr int NL = Path::NL;
-    const int lane = threadIdx.x;
-    const int u = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
     const int S = a.num_seqs;
     const int W = a.num_units;
+    const int R = a.rows;
+    const int Wr = a.aligned ? W / R : 0;       // units per row (aligned split)
+    const int Wrun = a.aligned ? Wr * R : W;    // units that can hold work
+    int u = blockIdx.x;
+    if constexpr (NW > 1) {
+        // NW rows of one range share a workgroup: wave w takes row (b % (R/NW)) NW + w
+        const int rg = R / NW;
+        const int wv = uni(static_cast<int>(threadIdx.x) >> 6);
+        u = ((static_cast<int>(blockIdx.x) % rg) * NW + wv) * Wr + static_cast<int>(blockIdx.x) / rg;
+    }
     const size_t pf = static_cast<size_t>((a.heads_per_row * D + ((2 * a.heads_per_row + 3) & ~3)));
-    // Sequences with no cached tokens get zeros; unit u covers sequences i == u (mod W).
-    for (int i = u; i < S; i += W)
-        if (ctx_of(a, i) == 0) write_zero_seq<T, D>(a, i, lane);
+    // Sequences with no cached tokens get zeros; unit u covers sequences i == u (mod Wrun).
+    if (u < Wrun)
+        for (int i = u; i < S; i += Wrun)
+            if (ctx_of(a, i) == 0) write_zero_seq<T, D>(a, i, lane);
     // Tiles per row.
     int mine = 0;
 #pragma unroll 4
     for (int i = lane; i < S; i += kWave) mine += tiles_of(ctx_of(a, i));
-    const int T_row = uni(wave_sum(mine));
+    int T_row = uni(wave_sum(mine));
+    if constexpr (NW > 1) {
+        // One count for the whole workgroup: its waves then run the same number of
+        // tiles and meet the per-tile barrier equally often, even if the lengths
+        // were changed while the kernel ran.
+        __shared__ int s_trow;
+        if (threadIdx.x == 0) s_trow = T_row;
+        __syncthreads();
+        T_row = s_trow;
+    }
     int32_t* rec = a.unit_rec + static_cast<size_t>(u) * kRecInts;
     if (lane == 0) rec[0] = -1;  // overwritten below when the unit holds work
-    const int total = a.rows * T_row;
-    const int C = (total + W - 1) / W;
-    const int start = u * C;
-    if (total == 0 || start >= total) return;
-    const int n_tiles = min(start + C, total) - start;
-    const int row0 = start / T_row;
-    const int tin = start - row0 * T_row;
+    int C, start, n_tiles, row0, tin;
+    if (a.aligned) {
+        // Every row is cut into the same Wr ranges of C tiles; unit (row r, range k)
+        // sits at line position r Wr C + k C, so the rows' ranges cover the same tiles.
+        C = (T_row + Wr - 1) / Wr;
+        row0 = u / Wr;
+        tin = (u - row0 * Wr) * C;
+        start = u * C;
+        n_tiles = u < Wrun ? min(C, T_row - tin) : 0;
+    } else {
+        const int total = R * T_row;
+        C = (total + W - 1) / W;
+        start = u * C;
+        n_tiles = min(start + C, total) - start;
+        row0 = T_row > 0 ? start / T_row : 0;
+        tin = start - row0 * T_row;
+    }
+    if (T_row == 0 || n_tiles <= 0) return;
     // Find the sequence holding tile `tin` of the row.
     int seq0 = 0, t00 = 0;
     {
@@ -626,6 +662,10 @@ __global__ __launch_bounds__(64) void decode_pass1(DecodeArgs a) {
         // HBM bandwidth than keeping two tiles in flight (the extra requests only
         // lengthen the memory queues); the unit count then sets the bytes in flight.
         wait_all_loads();
+        // The rows of a workgroup walk the same tiles; meeting once per tile keeps
+        // their requests for one block's adjacent heads (consecutive 4 KiB pieces of
+        // K and of V) reaching memory together.
+        if constexpr (NW > 1) __syncthreads();
         while (kf == ch.n) {  // chunk used up: describe the next tiles (empty chunks only
                               // arise from runs of sequences with no cached tokens)
             if (ch.next.row >= a.rows) {
@@ -725,6 +765,7 @@ template <typename T, int D, int GH>
 __global__ __launch_bounds__(64) void decode_pass2(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int u = blockIdx.x;
+    if (a.aligned && u >= (a.num_units / a.rows) * a.rows) return;  // never ran pass 1
     const int32_t* rec = a.unit_rec + static_cast<size_t>(u) * kRecInts;
     const int row = rec[0];
     if (row < 0) return;
@@ -753,7 +794,15 @@ hipError_t launch_pass2(const DecodeArgs& a, hipStream_t st) {
 template <class Path, typename T, int D>
 hipError_t launch_two_pass(const DecodeArgs& a, int passes, hipStream_t st) {
     if (passes & 1) {
-        hipLaunchKernelGGL((decode_pass1<Path, T, D>), dim3(a.num_units), dim3(kWave), 0, st, a);
+        const int nw = a.waves_per_group;
+        const int groups = nw > 1 ? (a.num_units / a.rows) * a.rows / nw : a.num_units;
+        switch (nw) {
+            case 1: hipLaunchKernelGGL((decode_pass1<Path, T, D, 1>), dim3(groups), dim3(kWave), 0, st, a); break;
+            case 2: hipLaunchKernelGGL((decode_pass1<Path, T, D, 2>), dim3(groups), dim3(2 * kWave), 0, st, a); break;
+            case 4: hipLaunchKernelGGL((decode_pass1<Path, T, D, 4>), dim3(groups), dim3(4 * kWave), 0, st, a); break;
+            case 8: hipLaunchKernelGGL((decode_pass1<Path, T, D, 8>), dim3(groups), dim3(8 * kWave), 0, st, a); break;
+            default: return hipErrorInvalidValue;
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

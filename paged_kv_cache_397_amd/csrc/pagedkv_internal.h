@@ -30,6 +30,8 @@ struct DecodeArgs {
     int32_t tiles_per_block;
     int32_t num_blocks;
     int32_t num_units;
+    int32_t aligned;            // 1: every row cut into num_units / rows identical ranges
+    int32_t waves_per_group;    // rows of one range per workgroup (aligned split only)
     float scale_log2e;          // scale * log2(e): scores are kept in base-2 units
 };
 
