@@ -5,7 +5,8 @@ One step is one pass of the whole decode hot path over the batch:
   host bookkeeping (library allocator: reserve every sequence's next slot,
   copy-on-write pairs, changed table entries) -> one host-to-device copy of
   that metadata -> block copies and table updates -> cache write of the new
-  tokens' K/V -> decode attention (pass 1, then the merge of split sequences).
+  tokens' K/V -> decode attention (one kernel: gather + attention, with the
+  merge of split sequences folded in).
 All inputs (cache contents, per-step q / k / v) are resident in HBM before the
 timed region.  The host part of step n+1 overlaps the device part of step n.
 
@@ -773,13 +774,12 @@ def main():
                                    block_tables=tables, table_updates=hu, lens_in=hc,
                                    lens_out=ctx_dev),
             ops.bind_decode(spec, out, qs[n], cache.k, cache.v, tables, ctx_dev, cfg.scale, units,
-                            ws, stage="partial"),
-            ops.bind_decode(spec, out, qs[n], cache.k, cache.v, tables, ctx_dev, cfg.scale, units,
-                            ws, stage="merge")))
+                            ws)))
 
     def step(n, mode):
-        """mode "warm": no timing events; "timed": events around pass 1 only (the
-        kernel the roofline is taken on); "profile": events around every launch."""
+        """mode "warm": no timing events; "timed": events around the decode kernel
+        only (the kernel the roofline is taken on); "profile": events around every
+        launch."""
         h0 = time.perf_counter()
         # a1: host bookkeeping in the library allocator
         st, done, slots, cows, nb, nc = cache.alloc.append_batch(seq_ids)
@@ -801,10 +801,10 @@ def main():
         pu[:, 2] = nb
         pp[:] = cows  # one (src, dst) row per token, (-1, -1) = no copy
         h1 = time.perf_counter()
-        append, partial, merge = calls[n]
+        append, decode = calls[n]
         timing = mode != "warm"
         if timing:
-            e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         if mode == "profile":
             e0.record(stream)
         # a3 + a4: copy-on-write block copies, the changed table entries, the cache
@@ -816,15 +816,12 @@ def main():
             e1 = torch.cuda.Event()
             e1.record(stream)
         ring_ev[r] = e1  # the ring slot is free again once the write launch has read it
-        # a5-a11: decode attention, pass 1 (gather + attention) then pass 2 (merge)
-        partial()
+        # a5-a11: decode attention, one kernel (gather + attention, split sequences
+        # merged by the last of their pieces to finish)
+        decode()
         if timing:
             e2.record(stream)
-        merge()
-        if mode == "profile":
-            e3.record(stream)
-        if timing:
-            ev[mode].append((e0, e1, e2, e3, int(ctx_now.sum())))
+            ev[mode].append((e0, e1, e2, int(ctx_now.sum())))
         if mode == "timed":
             host.append((h1 - h0, time.perf_counter() - h0))
 
@@ -851,33 +848,39 @@ def main():
         step(n, "profile")
     torch.cuda.synchronize()
     gc.enable()
-    # Cold pass 1: the last step's pass 1 run again (it reads the cache and writes
-    # only its outputs, so nothing changes) right after writing a 1 GiB buffer, more
-    # than the 256 MB MALL and every XCD's L2, so that its K/V come from HBM.
+    # Cold decode: the last step's decode run again (it reads the cache and writes
+    # only its outputs, so nothing changes) after a 1 GiB pass, more than the 256 MB
+    # MALL and every XCD's L2, so that its K/V come from HBM.  Two ways: right after
+    # writing the buffer (the MALL then holds dirty lines that the decode's reads
+    # evict and write back) and right after reading it (clean lines only).
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    _, last_partial, _ = calls[total_steps - 1]
-    cold = []
-    for _ in range(5):
-        flush.fill_(1.0)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        last_partial()
-        c1.record(stream)
-        torch.cuda.synchronize()
-        cold.append(c0.elapsed_time(c1) * 1e-3)
+    flush.fill_(1.0)
+    _, last_decode = calls[total_steps - 1]
+    cold = {"write": [], "read": []}
+    for kind in ("write", "read"):
+        for _ in range(5):
+            if kind == "write":
+                flush.fill_(1.0)
+            else:
+                flush.amax()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            last_decode()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold[kind].append(c0.elapsed_time(c1) * 1e-3)
     del flush
     cold_bytes = float(ctx_now.sum()) * kv_per_tok
 
-    tok = np.array([e[4] for e in ev["timed"]], dtype=np.float64)
+    tok = np.array([e[3] for e in ev["timed"]], dtype=np.float64)
     kv_bytes = tok * kv_per_tok
-    t_p1 = np.array([e[1].elapsed_time(e[2]) for e in ev["timed"]]) * 1e-3
+    t_dec = np.array([e[1].elapsed_time(e[2]) for e in ev["timed"]]) * 1e-3
     pe = ev["profile"]
-    pbytes = np.array([e[4] for e in pe], dtype=np.float64) * kv_per_tok
+    pbytes = np.array([e[3] for e in pe], dtype=np.float64) * kv_per_tok
     t_write = np.array([e[0].elapsed_time(e[1]) for e in pe]) * 1e-3
-    t_pp1 = np.array([e[1].elapsed_time(e[2]) for e in pe]) * 1e-3
-    t_attn = np.array([e[1].elapsed_time(e[3]) for e in pe]) * 1e-3
+    t_attn = np.array([e[1].elapsed_time(e[2]) for e in pe]) * 1e-3
     value = float(kv_bytes.sum() / wall / 1e9)
-    p1_gbps = float(np.median(kv_bytes / t_p1) / 1e9)
+    dec_gbps = float(np.median(kv_bytes / t_dec) / 1e9)
     unique = None
     if cfg.ctx_kind == "shared_prefix":
         # Shared blocks are read by many sequences in one pass; count each physical
@@ -917,36 +920,38 @@ def main():
             "note": f"{len(pe)} untimed steps after the timed region, events around every launch",
             "device_us_per_step_median": round(float(np.median(t_write + t_attn)) * 1e6, 2),
             "write_us_median": round(float(np.median(t_write)) * 1e6, 2),
-            "pass1_us_median": round(float(np.median(t_pp1)) * 1e6, 2),
             "attn_us_median": round(float(np.median(t_attn)) * 1e6, 2),
-            "pass2_us_median": round(float(np.median(t_attn - t_pp1)) * 1e6, 2),
             "attn_gbps_median": round(float(np.median(pbytes / t_attn) / 1e9), 2),
         },
-        "cold_pass1": {
-            "note": "the last step's pass 1 after writing a 1 GiB buffer (MALL and L2 flushed), 5 runs",
-            "us_median": round(float(np.median(cold)) * 1e6, 2),
-            "gbps_median": round(cold_bytes / float(np.median(cold)) / 1e9, 2),
+        "cold_decode": {
+            "note": "the last step's decode after a 1 GiB pass (MALL and L2 flushed), 5 runs each: "
+                    "after writing the buffer (dirty lines written back during the decode) and "
+                    "after reading it",
+            "after_write_us_median": round(float(np.median(cold["write"])) * 1e6, 2),
+            "after_write_gbps_median": round(cold_bytes / float(np.median(cold["write"])) / 1e9, 2),
+            "after_read_us_median": round(float(np.median(cold["read"])) * 1e6, 2),
+            "after_read_gbps_median": round(cold_bytes / float(np.median(cold["read"])) / 1e9, 2),
         },
         # useful matrix-core work of the grouped-query product (G > 1 runs on MFMA):
-        # 4 Hq D flops per cached token, over pass 1's median time
-        "mfma": ({"useful_tflops": round(4.0 * Hq * D * float(np.median(tok)) / float(np.median(t_p1)) / 1e12, 2),
-                  "frac_of_bf16_peak": round(4.0 * Hq * D * float(np.median(tok)) / float(np.median(t_p1))
+        # 4 Hq D flops per cached token, over the decode kernel's median time
+        "mfma": ({"useful_tflops": round(4.0 * Hq * D * float(np.median(tok)) / float(np.median(t_dec)) / 1e12, 2),
+                  "frac_of_bf16_peak": round(4.0 * Hq * D * float(np.median(tok)) / float(np.median(t_dec))
                                              / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
                  if Hq > Hkv and cfg.dtype == "bf16" else None),
         "host_bookkeeping_us_median": round(float(np.median([h[0] for h in host])) * 1e6, 2),
         "host_step_us_median": round(float(np.median([h[1] for h in host])) * 1e6, 2),
         "host_step_us_max": round(float(np.max([h[1] for h in host])) * 1e6, 2),
         "roofline": {
-            "kernel": "decode_pass1",
+            "kernel": "decode_pass1 (gather + attention, merge of split sequences folded in)",
             "bound": "hbm",
-            "achieved": round(p1_gbps, 2),
+            "achieved": round(dec_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(p1_gbps / HBM_PEAK_GBPS, 4),
+            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(cfg.name),
-            "pass1_us_mean": round(float(t_p1.mean()) * 1e6, 2),
-            "pass1_us_median": round(float(np.median(t_p1)) * 1e6, 2),
-            "pass1_us_max": round(float(np.max(t_p1)) * 1e6, 2),
+            "decode_us_mean": round(float(t_dec.mean()) * 1e6, 2),
+            "decode_us_median": round(float(np.median(t_dec)) * 1e6, 2),
+            "decode_us_max": round(float(np.max(t_dec)) * 1e6, 2),
             "algorithmic_bytes_per_launch": int(np.median(kv_bytes)),
         },
     }

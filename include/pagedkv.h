@@ -180,10 +180,15 @@ pa_status pa_append_tokens(const pa_cache_desc* desc, const void* k, const void*
  *                  so results are bit-reproducible for a given
  *                  (context_lens, num_units) and independent of block IDs.
  *   workspace      device scratch of at least pa_decode_workspace_bytes()
- *                  bytes, 16-B aligned, owned by the caller (no initial contents
- *                  needed); it holds partial results between the two kernels
- *                  of one call, so calls that share a workspace must be ordered
- *                  on one stream.
+ *                  bytes, 16-B aligned, owned by the caller.  It holds partial
+ *                  results and, in its last 4 * num_units bytes, one arrival
+ *                  count per unit.  Zero-fill it once after allocating it: the
+ *                  counts must be zero when a call starts, and every completed
+ *                  pa_paged_attn_decode call leaves them zero.  Pass the same
+ *                  workspace_bytes on every call that uses one workspace (the
+ *                  counts are found from its end), and order those calls on one
+ *                  stream.  _partial and _merge below never touch the counts and
+ *                  need no initial contents.
  * Block IDs outside [0, N) in a column that is read are replaced by 0.
  * Supported: bf16 with G in {1, 2, 4, 8, 16}; f32 with any G.  Outputs are
  * rounded to the output dtype nearest-even from fp32 accumulators.
@@ -202,16 +207,18 @@ pa_status pa_paged_attn_decode(const pa_cache_desc* desc, void* out, const void*
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * pa_paged_attn_decode enqueues two kernels.  The first gathers and attends:
- * each wave takes an equal range of the batch's 16-token tiles, writes the
- * sequences it holds whole to `out` and leaves partial (max, sum, accumulator)
- * records for sequences cut by range ends.  The second merges the records of
- * every cut sequence with the log-sum-exp rule ([P1] section 2.2 names only the
+ * pa_paged_attn_decode enqueues one kernel.  It gathers and attends: each wave
+ * takes an equal range of the batch's 16-token tiles, writes the sequences it
+ * holds whole to `out` and leaves partial (max, sum, accumulator) records for
+ * sequences cut by range ends.  The holder of a cut sequence's pieces that
+ * finishes last (found with the workspace's arrival counts) merges the records
+ * with the log-sum-exp rule, in piece order ([P1] section 2.2 names only the
  * gather; the split and the merge are this library's).
  *
- * The two kernels as separate calls, same arguments: _partial, then _merge on
- * one stream is exactly pa_paged_attn_decode (bit-identical outputs); it lets a
- * caller time or overlap the two stages.
+ * The same work as two kernels, same arguments: _partial (gather and attend,
+ * records only) then _merge (a second kernel merges every cut sequence) on one
+ * stream gives outputs bit-identical to pa_paged_attn_decode; it lets a caller
+ * time the stages apart.
  */
 pa_status pa_paged_attn_decode_partial(const pa_cache_desc* desc, void* out, const void* q,
                                        const void* k_cache, const void* v_cache,

@@ -37,7 +37,10 @@ bool group_kernel_for(const pa_cache_desc* d, int32_t group) {
     return d->dtype == PA_DTYPE_BF16 && group > 1;
 }
 
-// Workspace of W units: partial records (two per unit) | unit records.
+// Workspace of W units: partial records (two per unit) | unit records, from the
+// start; W split counts, from the end (count i is the i-th int32 before the end), so
+// that calls with different unit counts on one workspace never write each other's
+// counts.
 struct WorkspaceLayout {
     size_t piece_floats;  // floats of one partial record
     size_t rec_offset;    // bytes to the unit records
@@ -51,7 +54,7 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t num_q_heads, in
     w.piece_floats = static_cast<size_t>(gh) * d->head_dim + ((2 * gh + 3) & ~3);
     const size_t pieces = static_cast<size_t>(units) * 2 * w.piece_floats * sizeof(float);
     w.rec_offset = (pieces + 255) & ~size_t(255);
-    w.bytes = w.rec_offset + static_cast<size_t>(units) * pkv::kRecInts * sizeof(int32_t);
+    w.bytes = w.rec_offset + static_cast<size_t>(units) * (pkv::kRecInts + 1) * sizeof(int32_t);
     return w;
 }
 
@@ -258,6 +261,7 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
         char* base = static_cast<char*>(workspace);
         a.pieces = reinterpret_cast<float*>(base);
         a.unit_rec = reinterpret_cast<int32_t*>(base + w.rec_offset);
+        a.split_count_end = reinterpret_cast<int32_t*>(base + (workspace_bytes & ~size_t(3)));
         a.heads_per_row = use_group ? group : 1;
     }
     a.num_seqs = num_seqs;
@@ -272,6 +276,7 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     // Aligned split: with at least one unit per row, every row is cut into the same
     // ranges, and the rows of a range (up to 8, a power of two dividing the row
     // count) share a workgroup.
+    a.fused = passes == 3 ? 1 : 0;
     a.aligned = units >= rows ? 1 : 0;
     a.waves_per_group = 1;
     if (a.aligned)

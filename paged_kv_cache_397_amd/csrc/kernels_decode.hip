@@ -42,6 +42,21 @@
 namespace pkv {
 namespace {
 
+// Partial records are written and read at device scope (write-through past this
+// XCD's L2, reads from the device-coherent level), so a record written by one
+// XCD can be merged by another in the same launch without cache maintenance.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev2(float* p, float lo, float hi) {
+    const uint64_t w = static_cast<uint64_t>(__float_as_uint(lo)) |
+                       (static_cast<uint64_t>(__float_as_uint(hi)) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------------------------
 // One 16-token tile folded into a group accumulator with the matrix cores.
 //
@@ -289,10 +304,10 @@ struct HeadPath {
 #pragma unroll
             for (int mm = 0; mm < NL; ++mm)
 #pragma unroll
-                for (int e = 0; e < E; ++e) rec[16 * E * mm + 16 * e + i] = st.acc[mm][e];
+                for (int e = 0; e < E; ++e) store_dev(rec + 16 * E * mm + 16 * e + i, st.acc[mm][e]);
             if (i == 0) {
-                rec[D] = st.m;
-                rec[D + 1] = L;
+                store_dev(rec + D, st.m);
+                store_dev(rec + D + 1, L);
             }
         }
     }
@@ -360,11 +375,13 @@ struct GroupPath {
             }
         } else {
 #pragma unroll
-            for (int g = 0; g < NG; ++g)
-                *reinterpret_cast<f32x4*>(rec + i * D + 16 * g + 4 * j) = st.acc[g];
+            for (int g = 0; g < NG; ++g) {
+                store_dev2(rec + i * D + 16 * g + 4 * j, st.acc[g][0], st.acc[g][1]);
+                store_dev2(rec + i * D + 16 * g + 4 * j + 2, st.acc[g][2], st.acc[g][3]);
+            }
             if (j == 0) {
-                rec[G * D + i] = st.m;
-                rec[G * D + G + i] = L;
+                store_dev(rec + G * D + i, st.m);
+                store_dev(rec + G * D + G + i, L);
             }
         }
     }
@@ -383,7 +400,7 @@ struct GroupPath {
 // and their weights come from the lanes holding the pairs (or from memory when a
 // split has more than 64 pairs).
 template <typename T, int D, int GH>
-__device__ void merge_pieces(const DecodeArgs& a, int row, int seq, int us, int ue, int slot_us,
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int row, int seq, int us, int ue, int slot_us,
                              int lane) {
     constexpr int K = GH * D / kWave;
     static_assert(K >= 1 && (GH * D) % kWave == 0 && kWave % GH == 0, "merge shape");
@@ -394,19 +411,31 @@ __device__ void merge_pieces(const DecodeArgs& a, int row, int seq, int us, int 
     };
     const int np = ue - us + 1;
     const int pairs = np * GH;
+    // Accumulators of NB pieces are requested at once (fewer when a lane holds many
+    // elements, to bound the registers); the sum runs in piece order either way.  The
+    // first NB are requested together with the (m, l) pairs below.
+    constexpr int NB = K >= 32 ? 1 : K >= 16 ? 2 : 4;
+    const int nb0 = min(NB, np);
+    float v0[NB][K];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+        const float* r = piece(us + min(t, nb0 - 1));
+#pragma unroll
+        for (int c = 0; c < K; ++c) v0[t][c] = t < nb0 ? load_dev(r + lane + kWave * c) : 0.f;
+    }
     // (m, l) of this lane's first pair; kept for the weights below
     float m0 = kNegInf, l0 = 0.f;
     if (lane < pairs) {
         const float* r = piece(us + lane / GH);
-        m0 = r[kMOff + lane % GH];
-        l0 = r[kMOff + GH + lane % GH];
+        m0 = load_dev(r + kMOff + lane % GH);
+        l0 = load_dev(r + kMOff + GH + lane % GH);
     }
     float M = m0, den = l0;
     for (int k = lane + kWave; k < pairs; k += kWave) {  // splits with more than 64 pairs
         const float* r = piece(us + k / GH);
-        const float m = r[kMOff + k % GH];
+        const float m = load_dev(r + kMOff + k % GH);
         const float mn = fmaxf(M, m);
-        den = den * fast_exp2(M - mn) + fast_exp2(m - mn) * r[kMOff + GH + k % GH];
+        den = den * fast_exp2(M - mn) + fast_exp2(m - mn) * load_dev(r + kMOff + GH + k % GH);
         M = mn;
     }
 #pragma unroll
@@ -426,23 +455,35 @@ __device__ void merge_pieces(const DecodeArgs& a, int row, int seq, int us, int 
         Mh[c] = __shfl(M, (kWave * c) / D);  // element c of this lane is lane + 64 c, head 64 c / D
         acc[c] = 0.f;
     }
-    int p = us;
-    for (; p + 4 <= ue + 1; p += 4) {
-        float v[4][K];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NB; ++t) {
+        if (t >= nb0) break;
+        const int pk = t * GH;
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            const int h = (kWave * c) / D;
+            const float w = pairs <= kWave ? __shfl(w0, pk + h)
+                                           : fast_exp2(load_dev(piece(us + t) + kMOff + h) - Mh[c]);
+            acc[c] = __builtin_fmaf(w, v0[t][c], acc[c]);
+        }
+    }
+    int p = us + nb0;
+    for (; p + NB <= ue + 1; p += NB) {
+        float v[NB][K];
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
             const float* r = piece(p + t);
 #pragma unroll
-            for (int c = 0; c < K; ++c) v[t][c] = r[lane + kWave * c];
+            for (int c = 0; c < K; ++c) v[t][c] = load_dev(r + lane + kWave * c);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NB; ++t) {
             const int pk = (p + t - us) * GH;
 #pragma unroll
             for (int c = 0; c < K; ++c) {
                 const int h = (kWave * c) / D;
                 const float w = pairs <= kWave ? __shfl(w0, pk + h)
-                                               : fast_exp2(piece(p + t)[kMOff + h] - Mh[c]);
+                                               : fast_exp2(load_dev(piece(p + t) + kMOff + h) - Mh[c]);
                 acc[c] = __builtin_fmaf(w, v[t][c], acc[c]);
             }
         }
@@ -451,12 +492,12 @@ __device__ void merge_pieces(const DecodeArgs& a, int row, int seq, int us, int 
         const float* r = piece(p);
         float v[K];
 #pragma unroll
-        for (int c = 0; c < K; ++c) v[c] = r[lane + kWave * c];
+        for (int c = 0; c < K; ++c) v[c] = load_dev(r + lane + kWave * c);
         const int pk = (p - us) * GH;
 #pragma unroll
         for (int c = 0; c < K; ++c) {
             const int h = (kWave * c) / D;
-            const float w = pairs <= kWave ? __shfl(w0, pk + h) : fast_exp2(r[kMOff + h] - Mh[c]);
+            const float w = pairs <= kWave ? __shfl(w0, pk + h) : fast_exp2(load_dev(r + kMOff + h) - Mh[c]);
             acc[c] = __builtin_fmaf(w, v[c], acc[c]);
         }
     }
@@ -656,12 +697,33 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     };
     Buf A, B;
 
+    // A split sequence's pieces sit in units us .. ue (in unit us in record slot
+    // slot_us, elsewhere in slot 0).  With the merge folded in (a.fused), each holder
+    // counts its arrival on the count of unit ue once its record is written; `old` (lane 0)
+    // is the count before it.  The holder that finds the other ue - us pieces there
+    // merges them and sets the count back to zero for the next call.
+    struct Split {
+        int old, us, ue, slot_us, row, seq;
+    };
+    Split first_split{};
+    bool has_first = false;
+    bool arrive_first = false;  // first_split's record written, its count not yet moved
+    // Count the first piece's arrival; every load and store of the wave has completed
+    // (the caller has just waited), so its record is visible.
+    auto arrive = [&]() {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0)
+            first_split.old = __hip_atomic_fetch_add(a.split_count_end - 1 - first_split.ue, 1,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        arrive_first = false;
+    };
     auto issue = [&](Buf& b) {
         // One tile in flight per wave: the previous tile's loads have all returned
         // before the next tile is requested.  Measured on MI355X, this sustains more
         // HBM bandwidth than keeping two tiles in flight (the extra requests only
         // lengthen the memory queues); the unit count then sets the bytes in flight.
         wait_all_loads();
+        if (arrive_first) arrive();
         // The rows of a workgroup walk the same tiles; meeting once per tile keeps
         // their requests for one block's adjacent heads (consecutive 4 KiB pieces of
         // K and of V) reaching memory together.
@@ -701,12 +763,12 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     // ---- compute side: the open piece
     typename Path::Acc st;
     int p_seq = -1, p_row = 0, p_t0 = 0, p_last = 0, p_ctx = 0, p_g0 = 0, npieces = 0;
-    auto close_piece = [&]() {
+    auto close_piece = [&](Split& sp, bool defer) -> bool {
         const int nts = tiles_of(p_ctx);
         const bool whole = (p_t0 == 0) && (p_last == nts - 1);
+        const int seq_begin = start + p_g0 - p_t0;
         float* prec = a.pieces + (static_cast<size_t>(u) * 2 + (npieces == 0 ? 0 : 1)) * pf;
         if (npieces == 0 && lane == 0) {
-            const int seq_begin = start + p_g0 - p_t0;
             rec[0] = p_row;
             rec[1] = p_seq;
             rec[2] = seq_begin;
@@ -715,10 +777,39 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         }
         Path::finish(a, st, p_row, p_seq, whole, prec, lane);
         ++npieces;
+        if (!a.fused || whole) return false;
+        sp.us = seq_begin / C;
+        sp.ue = (seq_begin + nts - 1) / C;
+        sp.slot_us = seq_begin == sp.us * C ? 0 : 1;
+        sp.row = p_row;
+        sp.seq = p_seq;
+        sp.old = 0;
+        if (defer) return true;  // counted after the next tile's wait (arrive below)
+        // The record's device-scope stores are complete before the count moves.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_all_loads();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0)
+            sp.old = __hip_atomic_fetch_add(a.split_count_end - 1 - sp.ue, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    };
+    auto merge_if_last = [&](const Split& sp) {
+        if (__builtin_amdgcn_readfirstlane(sp.old) != sp.ue - sp.us) return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        merge_pieces<T, D, Path::GH>(a, sp.row, sp.seq, sp.us, sp.ue, sp.slot_us, lane);
+        if (lane == 0)
+            __hip_atomic_store(a.split_count_end - 1 - sp.ue, 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     };
     auto enter = [&](const Buf& b, int g) {
         if (b.opens) {
-            if (p_seq >= 0) close_piece();
+            // Only a unit's first piece can close inside the loop as a split one (it
+            // began in an earlier unit); its merge waits until the tiles are done.
+            if (p_seq >= 0 && close_piece(first_split, true)) {
+                has_first = true;
+                arrive_first = true;
+            }
 #pragma unroll
             for (int s = 0; s < NL; ++s) q.v[s] = qn.v[s];
             Path::reset(st);
@@ -754,7 +845,14 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     } else {
         Path::tile(a, st, q, A.k, A.v, A.r.tile, A.r.ctx, lane);
     }
-    close_piece();
+    if (arrive_first) {
+        wait_all_loads();
+        arrive();
+    }
+    Split last_split{};
+    const bool has_last = close_piece(last_split, false);
+    if (has_first) merge_if_last(first_split);
+    if (has_last) merge_if_last(last_split);
 }
 
 // ---------------------------------------------------------------------------------
@@ -806,7 +904,7 @@ hipError_t launch_two_pass(const DecodeArgs& a, int passes, hipStream_t st) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (passes & 2) {
+    if ((passes & 2) && !a.fused) {
         hipLaunchKernelGGL((decode_pass2<T, D, Path::GH>), dim3(a.num_units), dim3(kWave), 0, st, a);
         return hipGetLastError();
     }

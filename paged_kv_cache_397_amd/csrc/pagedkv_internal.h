@@ -20,6 +20,8 @@ struct DecodeArgs {
     const int32_t* context_lens;  // [S]
     float* pieces;              // [units][2][piece_floats]
     int32_t* unit_rec;          // [units][kRecInts]
+    int32_t* split_count_end;   // arrivals per split sequence (merge folded in): the
+                                // count of the split ending in unit u is split_count_end[-1 - u]
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -32,6 +34,7 @@ struct DecodeArgs {
     int32_t num_units;
     int32_t aligned;            // 1: every row cut into num_units / rows identical ranges
     int32_t waves_per_group;    // rows of one range per workgroup (aligned split only)
+    int32_t fused;              // 1: pass 1 merges split sequences itself (no pass 2)
     float scale_log2e;          // scale * log2(e): scores are kept in base-2 units
 };
 

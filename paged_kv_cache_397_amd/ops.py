@@ -181,7 +181,9 @@ def decode_workspace_bytes(spec: CacheSpec, num_q_heads: int, num_units: int = 0
 
 
 def decode_workspace(spec: CacheSpec, num_q_heads: int, num_units: int = 0, device="cuda"):
-    return torch.empty(decode_workspace_bytes(spec, num_q_heads, num_units), dtype=torch.uint8,
+    """Zero-filled once: the single-call decode needs its split counts at zero before
+    its first use (every completed call leaves them zero again)."""
+    return torch.zeros(decode_workspace_bytes(spec, num_q_heads, num_units), dtype=torch.uint8,
                        device=device)
 
 

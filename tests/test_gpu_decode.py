@@ -217,7 +217,9 @@ def test_partial_then_merge_equals_single_call_bitwise(dtype, Hq, Hkv, D, units)
 
 def test_reused_workspace_across_calls():
     """One workspace serves many calls with different lengths and unit counts, and
-    every output of every call is written (outputs start as NaN)."""
+    every output of every call is written (outputs start as NaN).  The arrival counts
+    at the workspace's end (one int32 per unit, read by the single-call decode) are
+    back at zero after every call."""
     spec = ops.CacheSpec(num_blocks=2048, block_size=16, num_kv_heads=8, head_dim=128, dtype="bf16")
     ws = ops.decode_workspace(spec, 32, 300)
     rng = gen.stream(52, 1)
@@ -229,6 +231,7 @@ def test_reused_workspace_across_calls():
             ops.paged_attn_decode(spec, out, b.q, b.cache.k, b.cache.v, b.tables, b.ctx_dev,
                                   1 / math.sqrt(128), units, ws)
             torch.cuda.synchronize()
+            assert int(ws[-4 * 300:].count_nonzero()) == 0, (trial, units)
             fresh = b.run(num_units=units)
             assert np.array_equal(to_storage(out).view(np.uint8), fresh.view(np.uint8)), (trial, units)
         assert_close(to_float64(fresh, "bf16"), b.expected(), "bf16", f"trial {trial}")
