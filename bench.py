@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gqa_b256",
-                    choices=["gqa_b256", "llama2_7b_b64", "shared_prefix_b16", "shared_prefix_b32",
+                    choices=["gqa_b256", "llama2_7b_b64", "tiny_f32", "shared_prefix_b16", "shared_prefix_b32",
                              "trace_13b", "trace_prefix", "prefill_13b", "prefill_gqa", "swap_13b", "blocksize_sweep"])
     ap.add_argument("--units", type=int, default=0, help="decode work units (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -467,6 +467,115 @@ def run_prefill(args):
     print(json.dumps(result), flush=True)
 
 
+def run_tiny(args):
+    """The tiny fp32 workload (4 sequences, ctx {1, 15, 16, 33}, 2 heads, D 64, a
+    16-block pool): the sequences are admitted, then every sequence's next token is
+    placed by the allocator (the third one takes a new block).  A step is that
+    write of 4 tokens (reshape_and_cache) plus decode over the lengths after it.
+    The same step is repeated (it rewrites the same slots with the same values), so
+    the pool never runs out; at 70 KB of K/V the step is bound by launch latency,
+    and its microseconds are the figure."""
+    import torch
+    from paged_kv_cache_397_amd import ops, _native
+    from paged_kv_cache_397_amd.batch import PagedKVCache, to_device
+    from workloads import CONFIGS, gen
+
+    _native.lib()
+    cfg = CONFIGS["tiny_f32"]
+    S, Hq, Hkv, D, B = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    spec = ops.CacheSpec(cfg.num_blocks, B, Hkv, D, cfg.dtype)
+    cache = PagedKVCache(spec, cfg.pool_order(), fill=0.0)
+    ctx0 = cfg.context_lens()
+    for i in range(S):
+        K, V = gen.seq_kv(cfg.seed, i, int(ctx0[i]), Hkv, D, cfg.dtype)
+        cache.add_sequence(i, K, V)
+    st, done, slots, cows, _, _ = cache.alloc.append_batch(np.arange(S, dtype=np.int64))
+    if st != 0 or done != S:
+        raise RuntimeError(f"append_batch failed: status {st}")
+    kn, vn = gen.new_tokens(cfg.seed, 1, S, Hkv, D, cfg.dtype)
+    k_new, v_new = to_device(kn, spec), to_device(vn, spec)
+    slots_dev = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).cuda()
+    tables, ctx_dev, _, ctx_h = cache.metadata(range(S))
+    q = to_device(gen.q_values(cfg.seed, 1, S, Hq, D, cfg.dtype), spec)
+    out = torch.empty(S, Hq, D, dtype=spec.torch_dtype, device="cuda")
+    ws = ops.decode_workspace(spec, Hq, 0)
+    stream = torch.cuda.current_stream()
+    write = ops.bind_reshape_and_cache(spec, k_new, v_new, slots_dev, cache.k, cache.v, stream)
+    decode = ops.bind_decode(spec, out, q, cache.k, cache.v, tables, ctx_dev, cfg.scale, 0, ws)
+    for _ in range(args.warmup):
+        write()
+        decode()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        write()
+        decode()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_w, t_d = [], []
+    for _ in range(100):  # per-launch durations, untimed
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        write()
+        b.record(stream)
+        decode()
+        c.record(stream)
+        torch.cuda.synchronize()
+        t_w.append(a.elapsed_time(b) * 1e-3)
+        t_d.append(b.elapsed_time(c) * 1e-3)
+    kv_bytes = float(ctx_h.sum()) * cfg.kv_bytes_per_token()
+    us = wall / args.steps * 1e6
+    result = {
+        "metric": "paged decode step latency (µs/step: cache write of the step's tokens + decode)",
+        "value": round(us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.title}", "seqs": S, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "block_size": B, "pool_blocks": cfg.num_blocks,
+                   "context_lens": [int(x) for x in ctx_h], "seed": cfg.seed},
+        "write_us": {"median": round(float(np.median(t_w)) * 1e6, 2), "min": round(float(np.min(t_w)) * 1e6, 2)},
+        "decode_us": {"median": round(float(np.median(t_d)) * 1e6, 2), "min": round(float(np.min(t_d)) * 1e6, 2)},
+        "kv_bytes_per_step": kv_bytes,
+        "decode_kv_gbps_median": round(kv_bytes / float(np.median(t_d)) / 1e9, 3),
+        "roofline": None,
+        "note": "launch-latency bound: 70 KB of K/V is far below any bandwidth or compute limit",
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on the host)")
+        from oracle.attention import paged_decode
+        from oracle.cache import reshape_and_cache
+        from oracle.layout import CacheLayout
+        lay = CacheLayout(cfg.num_blocks, Hkv, B, D, cfg.dtype)
+        kc, vc = lay.empty_cache(), lay.empty_cache()
+        t_host = tables.cpu().numpy().astype(np.int64)
+        for i in range(S):
+            L = int(ctx0[i])
+            K, V = gen.seq_kv(cfg.seed, i, L, Hkv, D, cfg.dtype)
+            reshape_and_cache(lay, K, V, t_host[i, np.arange(L) // B] * B + np.arange(L) % B, kc, vc)
+        q_h = gen.q_values(cfg.seed, 1, S, Hq, D, cfg.dtype)
+        times = []
+        for _ in range(1000):
+            h0 = time.perf_counter()
+            reshape_and_cache(lay, kn, vn, np.asarray(slots, dtype=np.int64), kc, vc)
+            paged_decode(lay, q_h, kc, vc, t_host, ctx_h.astype(np.int64), cfg.scale)
+            times.append(time.perf_counter() - h0)
+        result["cpu_baseline"] = {"value": round(float(np.median(times)) * 1e6, 2), "unit": "us/step",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": "the whole step (cache write of 4 tokens + fp64 decode of the 4 "
+                                            "sequences), median of 1000 runs"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def run_blocksize(args):
     """Block-size sweep.  Host: KV utilisation (tokens held / slots reserved) of the
     serving trace's running requests with on-demand paging at B = 8, 16, 32, 64,
@@ -674,6 +783,9 @@ def main():
     if args.config == "blocksize_sweep":
         run_blocksize(args)
         return
+    if args.config == "tiny_f32":
+        run_tiny(args)
+        return
     import torch
     from paged_kv_cache_397_amd import ops, _native
     from paged_kv_cache_397_amd.batch import PagedKVCache, to_device
@@ -778,8 +890,10 @@ def main():
 
     def step(n, mode):
         """mode "warm": no timing events; "timed": events around the decode kernel
-        only (the kernel the roofline is taken on); "profile": events around every
-        launch."""
+        (the kernel the roofline is taken on) on every 5th step; "profile": events
+        around every launch.  A marker between the write and the decode launch delays
+        the decode (measured: 2.3 us per step), so the other steps record only the
+        ring-slot event, after the decode."""
         h0 = time.perf_counter()
         # a1: host bookkeeping in the library allocator
         st, done, slots, cows, nb, nc = cache.alloc.append_batch(seq_ids)
@@ -802,7 +916,7 @@ def main():
         pp[:] = cows  # one (src, dst) row per token, (-1, -1) = no copy
         h1 = time.perf_counter()
         append, decode = calls[n]
-        timing = mode != "warm"
+        timing = mode == "profile" or (mode == "timed" and (n - warm) % 5 == 0)
         if timing:
             e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         if mode == "profile":
@@ -812,20 +926,22 @@ def main():
         append()
         if timing:
             e1.record(stream)
-        else:
-            e1 = torch.cuda.Event()
-            e1.record(stream)
-        ring_ev[r] = e1  # the ring slot is free again once the write launch has read it
         # a5-a11: decode attention, one kernel (gather + attention, split sequences
         # merged by the last of their pieces to finish)
         decode()
         if timing:
             e2.record(stream)
             ev[mode].append((e0, e1, e2, int(ctx_now.sum())))
+        else:
+            e2 = torch.cuda.Event()
+            e2.record(stream)
+        ring_ev[r] = e2  # the ring slot is free again once the step's launches are done
         if mode == "timed":
+            step_tok.append(int(ctx_now.sum()))
             host.append((h1 - h0, time.perf_counter() - h0))
 
     ev = {"timed": [], "profile": []}
+    step_tok = []  # sum of context lengths of every timed step
     # A full collection of the interpreter's heap (hundreds of thousands of objects
     # once torch is imported) stalls the host for tens of milliseconds and leaves the
     # GPU without work; settle the heap now and keep the collector off while stepping.
@@ -872,15 +988,17 @@ def main():
     del flush
     cold_bytes = float(ctx_now.sum()) * kv_per_tok
 
-    tok = np.array([e[3] for e in ev["timed"]], dtype=np.float64)
+    tok = np.array(step_tok, dtype=np.float64)  # every timed step
     kv_bytes = tok * kv_per_tok
+    s_tok = np.array([e[3] for e in ev["timed"]], dtype=np.float64)  # the sampled steps
+    s_bytes = s_tok * kv_per_tok
     t_dec = np.array([e[1].elapsed_time(e[2]) for e in ev["timed"]]) * 1e-3
     pe = ev["profile"]
     pbytes = np.array([e[3] for e in pe], dtype=np.float64) * kv_per_tok
     t_write = np.array([e[0].elapsed_time(e[1]) for e in pe]) * 1e-3
     t_attn = np.array([e[1].elapsed_time(e[2]) for e in pe]) * 1e-3
     value = float(kv_bytes.sum() / wall / 1e9)
-    dec_gbps = float(np.median(kv_bytes / t_dec) / 1e9)
+    dec_gbps = float(np.median(s_bytes / t_dec) / 1e9)
     unique = None
     if cfg.ctx_kind == "shared_prefix":
         # Shared blocks are read by many sequences in one pass; count each physical
@@ -934,8 +1052,8 @@ def main():
         },
         # useful matrix-core work of the grouped-query product (G > 1 runs on MFMA):
         # 4 Hq D flops per cached token, over the decode kernel's median time
-        "mfma": ({"useful_tflops": round(4.0 * Hq * D * float(np.median(tok)) / float(np.median(t_dec)) / 1e12, 2),
-                  "frac_of_bf16_peak": round(4.0 * Hq * D * float(np.median(tok)) / float(np.median(t_dec))
+        "mfma": ({"useful_tflops": round(4.0 * Hq * D * float(np.median(s_tok)) / float(np.median(t_dec)) / 1e12, 2),
+                  "frac_of_bf16_peak": round(4.0 * Hq * D * float(np.median(s_tok)) / float(np.median(t_dec))
                                              / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
                  if Hq > Hkv and cfg.dtype == "bf16" else None),
         "host_bookkeeping_us_median": round(float(np.median([h[0] for h in host])) * 1e6, 2),
@@ -952,7 +1070,11 @@ def main():
             "decode_us_mean": round(float(t_dec.mean()) * 1e6, 2),
             "decode_us_median": round(float(np.median(t_dec)) * 1e6, 2),
             "decode_us_max": round(float(np.max(t_dec)) * 1e6, 2),
-            "algorithmic_bytes_per_launch": int(np.median(kv_bytes)),
+            "timed_steps_sampled": len(t_dec),
+            "note": "HIP events on the launch stream around the decode launch of every 5th timed "
+                    "step; the interval starts at a marker after the write kernel, so it also holds "
+                    "the dispatch gap before the decode (rocprofv3 kernel durations are in profiles/)",
+            "algorithmic_bytes_per_launch": int(np.median(s_bytes)),
         },
     }
     if not args.no_cpu_baseline:

@@ -289,6 +289,20 @@ class BoundCall:
             N.check(st, self._name)
 
 
+def bind_reshape_and_cache(spec: CacheSpec, k, v, slot_mapping, k_cache, v_cache,
+                           stream=None) -> BoundCall:
+    """reshape_and_cache with its arguments fixed (same meaning as reshape_and_cache)."""
+    T = slot_mapping.numel()
+    if tuple(k.shape) != (T, spec.num_kv_heads, spec.head_dim) or k.shape != v.shape:
+        raise ValueError("k and v must be [T, Hkv, D]")
+    desc = spec.desc()
+    return BoundCall("pa_reshape_and_cache", (
+        ctypes.byref(desc), _dev(k, "k", spec.torch_dtype), _dev(v, "v", spec.torch_dtype),
+        _dev(slot_mapping, "slot_mapping", torch.int64), T,
+        _dev(k_cache, "k_cache", spec.torch_dtype), _dev(v_cache, "v_cache", spec.torch_dtype),
+        _stream(stream)), keep=desc)
+
+
 def bind_append_tokens(spec: CacheSpec, k, v, slot_mapping, k_cache, v_cache, cow_pairs=None,
                        block_tables=None, table_updates=None, lens_in=None, lens_out=None,
                        stream=None) -> BoundCall:
