@@ -76,6 +76,26 @@ def test_decode_matches_oracle(dtype, D, B, Hq, Hkv, units):
     assert not to_float64(out[0], dtype).any()          # ctx 0 -> zeros
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv,units", [("bf16", 16, 4, 0), ("bf16", 16, 4, 7),
+                                                 ("bf16", 8, 8, 0), ("f32", 4, 2, 64)])
+def test_batch_past_the_register_held_lengths(dtype, Hq, Hkv, units):
+    """300 sequences: the kernel scans the context lengths 64 at a time, so a unit's
+    first sequence is found several rounds into the scan, past the batch sizes of the
+    other tests.  Zero-length sequences (also at 256 and 257) get zeros; every other
+    output matches the oracle."""
+    rng = gen.stream(61, 1)
+    ctx = rng.integers(1, 80, 300)
+    ctx[[0, 100, 255, 256, 257, 299]] = 0
+    ctx[[1, 254, 258, 298]] = [700, 513, 640, 1]
+    spec = ops.CacheSpec(num_blocks=2048, block_size=16, num_kv_heads=Hkv, head_dim=64, dtype=dtype)
+    b = Batch(spec, ctx, Hq, seed=62, free_order=gen.pool_permutation(9, 2048))
+    out = b.run(num_units=units)
+    got = to_float64(out, dtype)
+    assert not np.isnan(got).any()
+    assert not got[ctx == 0].any()
+    assert_close(got, b.expected(), dtype, f"{dtype} G{Hq // Hkv} units {units} S 300")
+
+
 @pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 4, 4), ("bf16", 8, 2), ("f32", 2, 2)])
 def test_single_token_returns_value_bitwise(dtype, Hq, Hkv):
     spec = ops.CacheSpec(num_blocks=8, block_size=16, num_kv_heads=Hkv, head_dim=128, dtype=dtype)
