@@ -136,19 +136,32 @@ __global__ __launch_bounds__(D) void append_tokens_kernel(
     const int tid = threadIdx.x;
     const int wg = blockIdx.y * gridDim.x + blockIdx.x;
     const int nwg = gridDim.x * gridDim.y;
-    for (int n = wg * D + tid; n < num_updates; n += nwg * D) {
+    // Every metadata element this thread needs is requested before any is used: read
+    // from pinned host memory, each dependent read would cost a host-link round trip.
+    const bool tok = t < num_tokens;
+    const int64_t slot = tok ? slots[t] : -1;
+    const int cow_src = (tok && cow) ? cow[2 * t] : -1;
+    const int cow_dst = (tok && cow) ? cow[2 * t + 1] : -1;
+    const int n0 = wg * D + tid;
+    const int ur = n0 < num_updates ? upd[3 * n0] : -1;
+    const int uc = n0 < num_updates ? upd[3 * n0 + 1] : -1;
+    const int ub = n0 < num_updates ? upd[3 * n0 + 2] : 0;
+    const int ln = n0 < num_lens ? lens_in[n0] : 0;
+    if (ur >= 0 && ur < rows && uc >= 0 && uc < cols) tables[static_cast<int64_t>(ur) * cols + uc] = ub;
+    if (n0 < num_lens) lens_out[n0] = ln;
+    for (int n = n0 + nwg * D; n < num_updates; n += nwg * D) {  // more entries than threads
         const int r = upd[3 * n], c = upd[3 * n + 1];
         if (r >= 0 && r < rows && c >= 0 && c < cols) tables[static_cast<int64_t>(r) * cols + c] = upd[3 * n + 2];
     }
-    for (int n = wg * D + tid; n < num_lens; n += nwg * D) lens_out[n] = lens_in[n];
-    if (t >= num_tokens) return;
+    for (int n = n0 + nwg * D; n < num_lens; n += nwg * D) lens_out[n] = lens_in[n];
+    if (!tok) return;
     const int tpb = block_size / kTile;
     const int64_t head_u4 = static_cast<int64_t>(tpb) * kTile * D * sizeof(T) / 16;  // one head of one block
     if (cow) {
-        const int src = cow[2 * t], dst = cow[2 * t + 1];
-        if (src >= 0 && src < num_blocks && dst >= 0 && dst < num_blocks && src != dst) {
-            const int64_t so = (static_cast<int64_t>(src) * num_kv_heads + h) * head_u4;
-            const int64_t dof = (static_cast<int64_t>(dst) * num_kv_heads + h) * head_u4;
+        if (cow_src >= 0 && cow_src < num_blocks && cow_dst >= 0 && cow_dst < num_blocks &&
+            cow_src != cow_dst) {
+            const int64_t so = (static_cast<int64_t>(cow_src) * num_kv_heads + h) * head_u4;
+            const int64_t dof = (static_cast<int64_t>(cow_dst) * num_kv_heads + h) * head_u4;
             const u32x4* ks = reinterpret_cast<const u32x4*>(k_cache) + so;
             const u32x4* vs = reinterpret_cast<const u32x4*>(v_cache) + so;
             u32x4* kd = reinterpret_cast<u32x4*>(k_cache) + dof;
@@ -162,7 +175,6 @@ __global__ __launch_bounds__(D) void append_tokens_kernel(
         }
         __syncthreads();
     }
-    const int64_t slot = slots[t];
     if (slot < 0 || slot >= static_cast<int64_t>(num_blocks) * block_size) return;
     const int64_t b = slot / block_size;
     const int o = static_cast<int>(slot - b * block_size);
