@@ -277,6 +277,7 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     // ranges, and the rows of a range (up to 8, a power of two dividing the row
     // count) share a workgroup.
     a.fused = passes == 3 ? 1 : 0;
+
     a.aligned = units >= rows ? 1 : 0;
     a.waves_per_group = 1;
     if (a.aligned)

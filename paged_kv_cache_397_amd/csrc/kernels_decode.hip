@@ -12,10 +12,12 @@
 // Work split ("units"): per work row (a KV head for the group kernel, a query
 // head for the per-head kernel) the sequences' 16-token tiles are laid end to
 // end.  With at least one unit per row, every row is cut into the same
-// num_units / rows ranges of C tiles (the aligned split), so the units of one
-// range cover the same tiles in every row; with fewer units than rows, the rows
-// are laid one after another and the whole line is cut into num_units equal
-// ranges.  One wavefront owns one range: even work whatever the length mix.
+// num_units / rows ranges (the aligned split), so the units of one range cover
+// the same tiles in every row.  The ranges are equal in cost, where a sequence
+// costs its tiles plus one tile for opening and closing its piece; with fewer
+// units than rows, the rows are laid one after another and the whole line is
+// cut into num_units ranges of equal tile count.  One wavefront owns one range:
+// even work whatever the length mix.
 // Under the aligned split, the rows of one range (up to eight) run as the waves
 // of one workgroup and meet once per tile, so the adjacent 4 KiB head slices of
 // a block are requested together.  A sequence that a range holds whole is
@@ -389,8 +391,7 @@ struct GroupPath {
 
 // ---------------------------------------------------------------------------------
 // Log-sum-exp merge of the partial records of one split (sequence, row), pieces
-// held by units us .. ue (unit us keeps it in record slot slot_us, the others
-// in slot 0):
+// held by units us .. ue (unit us keeps it in record slot 1, the others in slot 0):
 //   M = max_p m_p;  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // GH heads share a row.  Pair k = (piece us + k / GH, head k % GH).  First each
 // lane folds its pairs' (m, l) with a running maximum; GH divides the wave width,
@@ -400,14 +401,14 @@ struct GroupPath {
 // and their weights come from the lanes holding the pairs (or from memory when a
 // split has more than 64 pairs).
 template <typename T, int D, int GH>
-__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int row, int seq, int us, int ue, int slot_us,
-                             int lane) {
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int row, int seq, int us, int ue,
+                                             int lane) {
     constexpr int K = GH * D / kWave;
     static_assert(K >= 1 && (GH * D) % kWave == 0 && kWave % GH == 0, "merge shape");
     constexpr int kMOff = GH * D;  // record: [GH][D] acc, [GH] m, [GH] l
     constexpr size_t pf = static_cast<size_t>(GH * D + ((2 * GH + 3) & ~3));
     auto piece = [&](int p) -> const float* {
-        return a.pieces + (static_cast<size_t>(p) * 2 + (p == us ? slot_us : 0)) * pf;
+        return a.pieces + (static_cast<size_t>(p) * 2 + (p == us ? 1 : 0)) * pf;
     };
     const int np = ue - us + 1;
     const int pairs = np * GH;
@@ -628,31 +629,92 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     if (u < Wrun)
         for (int i = u; i < S; i += Wrun)
             if (ctx_of(a, i) == 0) write_zero_seq<T, D>(a, i, lane);
-    // Tiles per row.
-    int mine = 0;
+    // Tiles per row, and their cost for the aligned split: a sequence with n > 0
+    // tiles costs kTileCost n + kPieceCost (opening and closing a piece takes time
+    // beyond its tiles).
+    constexpr int pcost = kPieceCost;
+    int mine_t = 0, mine_w = 0;
 #pragma unroll 4
-    for (int i = lane; i < S; i += kWave) mine += tiles_of(ctx_of(a, i));
-    int T_row = uni(wave_sum(mine));
+    for (int i = lane; i < S; i += kWave) {
+        const int n = tiles_of(ctx_of(a, i));
+        mine_t += n;
+        mine_w += n > 0 ? kTileCost * n + pcost : 0;
+    }
+    int T_row = uni(wave_sum(mine_t));
+    int W_row = uni(wave_sum(mine_w));
     if constexpr (NW > 1) {
         // One count for the whole workgroup: its waves then run the same number of
         // tiles and meet the per-tile barrier equally often, even if the lengths
         // were changed while the kernel ran.
-        __shared__ int s_trow;
-        if (threadIdx.x == 0) s_trow = T_row;
+        __shared__ int s_tw[2];
+        if (threadIdx.x == 0) {
+            s_tw[0] = T_row;
+            s_tw[1] = W_row;
+        }
         __syncthreads();
-        T_row = s_trow;
+        T_row = s_tw[0];
+        W_row = s_tw[1];
     }
     int32_t* rec = a.unit_rec + static_cast<size_t>(u) * kRecInts;
-    if (lane == 0) rec[0] = -1;  // overwritten below when the unit holds work
-    int C, start, n_tiles, row0, tin;
+    if (lane == 0) rec[0] = -1;  // set below when a split sequence ends in this unit
+    // The unit's tiles: n_tiles from tile tin of row row0, starting in sequence seq0 at
+    // its tile t00.  first_*: units holding the first and last tile of the sequence the
+    // unit's first piece belongs to, when that piece starts inside it (else -1);
+    // last_*: the same for the last piece, when it runs past the unit's end.
+    int n_tiles = 0, row0 = 0, tin = 0, seq0 = 0, t00 = 0;
+    int C = 0, start = 0;  // one-line split
+    int first_us = -1, first_ue = -1, last_us = -1, last_ue = -1;
     if (a.aligned) {
-        // Every row is cut into the same Wr ranges of C tiles; unit (row r, range k)
-        // sits at line position r Wr C + k C, so the rows' ranges cover the same tiles.
-        C = (T_row + Wr - 1) / Wr;
+        // Every row is cut into the same Wr ranges of CC cost units; range k covers
+        // the tiles whose cost starts at or after k CC and before (k + 1) CC.  The tile
+        // at cost b, in sequence i with cost prefix P_i, tile prefix S_i and n_i tiles,
+        // is S_i + clamp(ceil((b - P_i - kPieceCost) / kTileCost), 0, n_i); tile t of
+        // sequence i lies in range floor((P_i + kPieceCost + kTileCost t) / CC).
+        // CC >= kTileCost: consecutive tiles of a sequence start kTileCost apart, so
+        // every range strictly between a split sequence's first and last range holds
+        // a tile of it, and the merge finds a piece in every unit from us to ue.
         row0 = u / Wr;
-        tin = (u - row0 * Wr) * C;
-        start = u * C;
-        n_tiles = u < Wrun ? min(C, T_row - tin) : 0;
+        const int k = u - row0 * Wr;
+        const int CC = max(kTileCost, (W_row + Wr - 1) / Wr);
+        const int b0 = k * CC;
+        const int b1 = min(b0 + CC, W_row);
+        if (u < Wrun && b0 < W_row) {
+            int tb0 = -1, tb1 = b1 >= W_row ? T_row : -1;
+            int carry_t = 0, carry_w = 0;
+            for (int base = 0; base < S && (tb0 < 0 || tb1 < 0); base += kWave) {
+                const int i = base + lane;
+                const int n = i < S ? tiles_of(ctx_of(a, i)) : 0;
+                const int w = n > 0 ? kTileCost * n + pcost : 0;
+                const int incl_t = wave_inclusive_scan(n, lane) + carry_t;
+                const int incl_w = wave_inclusive_scan(w, lane) + carry_w;
+                auto locate = [&](int b, int& tb, int& seq, int& t, int& us, int& ue) {
+                    const unsigned long long hit = __ballot(incl_w > b);
+                    if (!hit) return;
+                    const int f = __ffsll(static_cast<long long>(hit)) - 1;
+                    const int nf = __builtin_amdgcn_readlane(n, f);
+                    const int pf_ = __builtin_amdgcn_readlane(incl_w - w, f);
+                    const int x = b - pf_ - pcost;
+                    t = min(x <= 0 ? 0 : (x + kTileCost - 1) / kTileCost, nf);
+                    tb = __builtin_amdgcn_readlane(incl_t - n, f) + t;
+                    seq = base + f;
+                    if (t > 0 && t < nf) {  // the boundary cuts sequence seq
+                        us = row0 * Wr + (pf_ + pcost) / CC;
+                        ue = row0 * Wr + (pf_ + pcost + kTileCost * (nf - 1)) / CC;
+                    }
+                };
+                int s_unused = 0, t_unused = 0;
+                if (tb0 < 0) locate(b0, tb0, seq0, t00, first_us, first_ue);
+                if (tb1 < 0) locate(b1, tb1, s_unused, t_unused, last_us, last_ue);
+                carry_t = __builtin_amdgcn_readlane(incl_t, kWave - 1);
+                carry_w = __builtin_amdgcn_readlane(incl_w, kWave - 1);
+            }
+            tin = tb0;
+            n_tiles = tb0 >= 0 && tb1 >= 0 ? tb1 - tb0 : 0;
+        }
+        first_us = uni(first_us);
+        first_ue = uni(first_ue);
+        last_us = uni(last_us);
+        last_ue = uni(last_ue);
     } else {
         const int total = R * T_row;
         C = (total + W - 1) / W;
@@ -660,26 +722,25 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         n_tiles = min(start + C, total) - start;
         row0 = T_row > 0 ? start / T_row : 0;
         tin = start - row0 * T_row;
-    }
-    if (T_row == 0 || n_tiles <= 0) return;
-    // Find the sequence holding tile `tin` of the row.
-    int seq0 = 0, t00 = 0;
-    {
-        int carry = 0;
-        for (int base = 0; base < S; base += kWave) {
-            const int i = base + lane;
-            const int n = i < S ? tiles_of(ctx_of(a, i)) : 0;
-            const int incl = wave_inclusive_scan(n, lane) + carry;
-            const unsigned long long hit = __ballot(incl > tin);
-            if (hit) {
-                const int f = __ffsll(static_cast<long long>(hit)) - 1;
-                seq0 = base + f;
-                t00 = tin - __shfl(incl - n, f);
-                break;
+        if (n_tiles > 0) {
+            // Find the sequence holding tile `tin` of the row.
+            int carry = 0;
+            for (int base = 0; base < S; base += kWave) {
+                const int i = base + lane;
+                const int n = i < S ? tiles_of(ctx_of(a, i)) : 0;
+                const int incl = wave_inclusive_scan(n, lane) + carry;
+                const unsigned long long hit = __ballot(incl > tin);
+                if (hit) {
+                    const int f = __ffsll(static_cast<long long>(hit)) - 1;
+                    seq0 = base + f;
+                    t00 = tin - __shfl(incl - n, f);
+                    break;
+                }
+                carry = __shfl(incl, kWave - 1);
             }
-            carry = __shfl(incl, kWave - 1);
         }
     }
+    if (T_row == 0 || n_tiles <= 0) return;
 
     const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
     const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
@@ -697,13 +758,13 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     };
     Buf A, B;
 
-    // A split sequence's pieces sit in units us .. ue (in unit us in record slot
-    // slot_us, elsewhere in slot 0).  With the merge folded in (a.fused), each holder
+    // A split sequence's pieces sit in units us .. ue (in unit us in record slot 1,
+    // elsewhere in slot 0).  With the merge folded in (a.fused), each holder
     // counts its arrival on the count of unit ue once its record is written; `old` (lane 0)
     // is the count before it.  The holder that finds the other ue - us pieces there
     // merges them and sets the count back to zero for the next call.
     struct Split {
-        int old, us, ue, slot_us, row, seq;
+        int old, us, ue, row, seq;
     };
     Split first_split{};
     bool has_first = false;
@@ -766,24 +827,36 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     auto close_piece = [&](Split& sp, bool defer) -> bool {
         const int nts = tiles_of(p_ctx);
         const bool whole = (p_t0 == 0) && (p_last == nts - 1);
-        const int seq_begin = start + p_g0 - p_t0;
-        float* prec = a.pieces + (static_cast<size_t>(u) * 2 + (npieces == 0 ? 0 : 1)) * pf;
-        if (npieces == 0 && lane == 0) {
-            rec[0] = p_row;
-            rec[1] = p_seq;
-            rec[2] = seq_begin;
-            rec[3] = seq_begin + nts;
-            rec[4] = C;
-        }
+        // A split piece's record goes to slot 1 when it holds its sequence's first
+        // tile (it is then its unit's last piece), else to slot 0 (its unit's first).
+        const int slot = p_t0 == 0 ? 1 : 0;
+        float* prec = a.pieces + (static_cast<size_t>(u) * 2 + slot) * pf;
         Path::finish(a, st, p_row, p_seq, whole, prec, lane);
         ++npieces;
-        if (!a.fused || whole) return false;
-        sp.us = seq_begin / C;
-        sp.ue = (seq_begin + nts - 1) / C;
-        sp.slot_us = seq_begin == sp.us * C ? 0 : 1;
+        if (whole) return false;
+        if (a.aligned) {
+            // only the first piece can start inside its sequence, only the last run on
+            sp.us = p_t0 > 0 ? first_us : last_us;
+            sp.ue = p_t0 > 0 ? first_ue : last_ue;
+        } else {
+            const int seq_begin = start + p_g0 - p_t0;
+            sp.us = seq_begin / C;
+            sp.ue = (seq_begin + nts - 1) / C;
+        }
+        // Units outside [0, Wrun) only arise if the lengths changed under the kernel:
+        // leave that split unmerged rather than address records that do not exist.
+        if (sp.us < 0 || sp.ue < sp.us || sp.ue >= Wrun) return false;
         sp.row = p_row;
         sp.seq = p_seq;
         sp.old = 0;
+        // For the two-kernel path: the split that ends in this unit is merged by it.
+        if (p_t0 > 0 && sp.ue == u && lane == 0) {
+            rec[0] = p_row;
+            rec[1] = p_seq;
+            rec[2] = sp.us;
+            rec[3] = sp.ue;
+        }
+        if (!a.fused) return false;
         if (defer) return true;  // counted after the next tile's wait (arrive below)
         // The record's device-scope stores are complete before the count moves.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -797,7 +870,7 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     auto merge_if_last = [&](const Split& sp) {
         if (__builtin_amdgcn_readfirstlane(sp.old) != sp.ue - sp.us) return;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        merge_pieces<T, D, Path::GH>(a, sp.row, sp.seq, sp.us, sp.ue, sp.slot_us, lane);
+        merge_pieces<T, D, Path::GH>(a, sp.row, sp.seq, sp.us, sp.ue, lane);
         if (lane == 0)
             __hip_atomic_store(a.split_count_end - 1 - sp.ue, 0, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -867,12 +940,9 @@ __global__ __launch_bounds__(64) void decode_pass2(DecodeArgs a) {
     const int32_t* rec = a.unit_rec + static_cast<size_t>(u) * kRecInts;
     const int row = rec[0];
     if (row < 0) return;
-    const int seq = rec[1], begin = rec[2], end = rec[3], C = rec[4];
-    if (seq < 0 || seq >= a.num_seqs || row >= a.rows || C <= 0 || begin < 0) return;
-    const int ustart = u * C;
-    if (begin >= ustart || end > ustart + C) return;
-    const int us = begin / C;
-    merge_pieces<T, D, GH>(a, row, seq, us, u, (begin == us * C) ? 0 : 1, lane);
+    const int seq = rec[1], us = rec[2], ue = rec[3];
+    if (seq < 0 || seq >= a.num_seqs || row >= a.rows || ue != u || us < 0 || us >= u) return;
+    merge_pieces<T, D, GH>(a, row, seq, us, u, lane);
 }
 
 template <typename T, int D>

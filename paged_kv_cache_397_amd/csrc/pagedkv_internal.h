@@ -59,7 +59,12 @@ struct PrefillArgs {
     float scale_log2e;
 };
 
-constexpr int kRecInts = 8;  // per-unit record: row, seq, seq_begin, seq_end, tiles_per_unit
+constexpr int kRecInts = 8;  // per-unit record: row, seq, first unit, last unit of the split ending there
+// Aligned split: a sequence with n tiles costs kTileCost n + kPieceCost.  Measured on
+// the batch-256 GQA workload, a unit's time grows by about 0.8 of a tile per extra
+// sequence (piece) in its range, so a piece is charged one tile.
+constexpr int kTileCost = 4;
+constexpr int kPieceCost = 4;
 
 // Floats of one partial-result record: heads_per_row * (D accumulators + max + sum).
 inline size_t piece_floats(int heads_per_row, int head_dim) {
