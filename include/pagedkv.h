@@ -54,11 +54,12 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
  * Layout (the library's own choice; the pages fix only the logical picture).
  * Let s = element bytes, X = 16 / s (elements per 16-byte group), E = X / 4,
  * TPB = block_size / 16.  A block is cut into TPB tiles of 16 tokens; tiles
- * are ordered block -> kv head -> tile, each tile holding 16 * head_dim
- * elements.  Element (block b, head h, token slot o, dim d) sits at
+ * are ordered block -> tile -> kv head (the Hkv heads' tiles of one tile slot
+ * are adjacent), each tile holding 16 * head_dim elements.  Element (block b,
+ * head h, token slot o, dim d) sits at
  *
- *   K: ((((b*Hkv + h)*TPB + o/16)*(D/X) + d/X)*16 + o%16)*X + d%X
- *   V: ((b*Hkv + h)*TPB + o/16)*16*D
+ *   K: ((((b*TPB + o/16)*Hkv + h)*(D/X) + d/X)*16 + o%16)*X + d%X
+ *   V: ((b*TPB + o/16)*Hkv + h)*16*D
  *      + ((((d/(16E))*4 + (o%16)/4)*16 + d%16)*E + (d/16)%E)*4 + o%4
  *
  * so a K 16-byte group is X consecutive dims of one token, and a V 16-byte

@@ -12,7 +12,8 @@ is this library's own contract, stated in ``include/pagedkv.h``:
 * K tile   = [D/X][16][X]          (X = 16 bytes / element size)
 * V tile   = [D/(16E)][4][16][E][4] (E = X/4): each 16-byte group holds four
   consecutive tokens of E head-dim positions spaced 16 apart;
-* tiles are ordered block -> kv head -> tile.
+* tiles are ordered block -> tile -> kv head (the Hkv heads' tiles of one tile
+  slot of a block are adjacent).
 
 This module expresses that contract as numpy reshapes/transposes of the flat
 cache arrays (no index arithmetic is shared with the HIP code).  Values stay in
@@ -91,16 +92,18 @@ class CacheLayout:
 
     # -- views of the flat arrays ---------------------------------------------
     def _k6(self, k_cache):
-        """K as [block, head, tile, d//X, token%16, d%X]."""
+        """K as [block, head, tile, d//X, token%16, d%X] (stored tile-major)."""
         N, H, T, D, X = (self.num_blocks, self.num_kv_heads, self.tiles_per_block,
                          self.head_dim, self.X)
-        return k_cache.reshape(N, H, T, D // X, TILE, X)
+        return k_cache.reshape(N, T, H, D // X, TILE, X).transpose(0, 2, 1, 3, 4, 5)
 
     def _v8(self, v_cache):
-        """V as [block, head, tile, m, j, i, e, r]: token 4j+r, dim 16E*m + 16e + i."""
+        """V as [block, head, tile, m, j, i, e, r]: token 4j+r, dim 16E*m + 16e + i
+        (stored tile-major)."""
         N, H, T, D, E = (self.num_blocks, self.num_kv_heads, self.tiles_per_block,
                          self.head_dim, self.E)
-        return v_cache.reshape(N, H, T, D // (TILE * E), 4, TILE, E, 4)
+        return v_cache.reshape(N, T, H, D // (TILE * E), 4, TILE, E, 4).transpose(
+            0, 2, 1, 3, 4, 5, 6, 7)
 
     # -- reads ----------------------------------------------------------------
     def gather(self, k_cache, v_cache, blocks, length):

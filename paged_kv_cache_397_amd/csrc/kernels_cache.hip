@@ -30,7 +30,7 @@ __global__ __launch_bounds__(D) void reshape_and_cache_kernel(
     const int o = static_cast<int>(slot - b * block_size);
     const int tpb = block_size / kTile;
     const size_t tile_base =
-        ((static_cast<size_t>(b) * num_kv_heads + h) * tpb + (o >> 4)) * (kTile * D);
+        ((static_cast<size_t>(b) * tpb + (o >> 4)) * num_kv_heads + h) * (kTile * D);
     const size_t src = (static_cast<size_t>(t) * num_kv_heads + h) * D;
     const int ti = o & 15;
     // V: 16-byte group (m, j, i) holds tokens 4j..4j+3 of dims 16E*m + 16e + i.
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict_
 // h's part of the block that token t's copy-on-write pair names (if any), then
 // scatters token t's K and V for head h; every workgroup applies its share of the
 // block-table updates and of the context-length copy.  A head's part of a block is
-// one contiguous region of each cache array (tiles are ordered block -> head ->
-// tile), so the copy and the token's write for that head never leave the workgroup.
+// its tile in each of the block's tile slots (tiles are ordered block -> tile ->
+// head), so the copy and the token's write for that head never leave the workgroup.
 // Another token's in-place write into the copy source can land before the copy
 // reads it; it is then carried into the copy at the offset the copying token itself
 // writes next (sequences that share a block hold the same number of tokens in it),
@@ -156,19 +156,22 @@ __global__ __launch_bounds__(D) void append_tokens_kernel(
     for (int n = n0 + nwg * D; n < num_lens; n += nwg * D) lens_out[n] = lens_in[n];
     if (!tok) return;
     const int tpb = block_size / kTile;
-    const int64_t head_u4 = static_cast<int64_t>(tpb) * kTile * D * sizeof(T) / 16;  // one head of one block
+    constexpr int tile_u4 = kTile * D * static_cast<int>(sizeof(T)) / 16;  // one tile of one head
     if (cow) {
         if (cow_src >= 0 && cow_src < num_blocks && cow_dst >= 0 && cow_dst < num_blocks &&
             cow_src != cow_dst) {
-            const int64_t so = (static_cast<int64_t>(cow_src) * num_kv_heads + h) * head_u4;
-            const int64_t dof = (static_cast<int64_t>(cow_dst) * num_kv_heads + h) * head_u4;
-            const u32x4* ks = reinterpret_cast<const u32x4*>(k_cache) + so;
-            const u32x4* vs = reinterpret_cast<const u32x4*>(v_cache) + so;
-            u32x4* kd = reinterpret_cast<u32x4*>(k_cache) + dof;
-            u32x4* vd = reinterpret_cast<u32x4*>(v_cache) + dof;
-            for (int64_t i = tid; i < head_u4; i += D) {
-                kd[i] = ks[i];
-                vd[i] = vs[i];
+            // head h's part of a block: its tile in each of the block's tpb tile slots
+            for (int tt = 0; tt < tpb; ++tt) {
+                const int64_t so = ((static_cast<int64_t>(cow_src) * tpb + tt) * num_kv_heads + h) * tile_u4;
+                const int64_t dof = ((static_cast<int64_t>(cow_dst) * tpb + tt) * num_kv_heads + h) * tile_u4;
+                const u32x4* ks = reinterpret_cast<const u32x4*>(k_cache) + so;
+                const u32x4* vs = reinterpret_cast<const u32x4*>(v_cache) + so;
+                u32x4* kd = reinterpret_cast<u32x4*>(k_cache) + dof;
+                u32x4* vd = reinterpret_cast<u32x4*>(v_cache) + dof;
+                for (int i = tid; i < tile_u4; i += D) {
+                    kd[i] = ks[i];
+                    vd[i] = vs[i];
+                }
             }
             // the copy's stores complete before any thread writes the token over them
             __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(D) void append_tokens_kernel(
     const int j = ti >> 2, r = ti & 3;
     const int d = tid;
     const size_t tile_base =
-        ((static_cast<size_t>(b) * num_kv_heads + h) * tpb + (o >> 4)) * (kTile * D);
+        ((static_cast<size_t>(b) * tpb + (o >> 4)) * num_kv_heads + h) * (kTile * D);
     const size_t src = (static_cast<size_t>(t) * num_kv_heads + h) * D;
     const int m = d / (16 * E), ee = (d >> 4) % E, i = d & 15;
     v_cache[tile_base + ((((m * 4 + j) * 16 + i) * E + ee) * 4 + r)] = v[src + d];

@@ -527,7 +527,7 @@ struct Chunk {
     int tile;    // lane k: tile index inside its sequence
     int row;     // lane k: work row
     int ctx;     // lane k: context length of its sequence
-    int toff;    // lane k: tile index in the cache, (block * Hkv + kv head) * tpb + tile % tpb
+    int toff;    // lane k: tile index in the cache, (block * tpb + tile % tpb) * Hkv + kv head
     Cursor next; // where the walk continues after the chunk (uniform)
 };
 
@@ -585,7 +585,7 @@ __device__ __forceinline__ Chunk build_chunk(const DecodeArgs& a, Cursor c, int 
         const int e = tin / tpb;
         int blk = a.block_tables[static_cast<size_t>(ssk) * a.max_blocks + e];
         blk = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
-        toff = (blk * a.num_kv_heads + Path::kv_head(a, rr)) * tpb + (tin - e * tpb);
+        toff = (blk * tpb + (tin - e * tpb)) * a.num_kv_heads + Path::kv_head(a, rr);
     }
     ch.toff = toff;
     // the walk after the chunk

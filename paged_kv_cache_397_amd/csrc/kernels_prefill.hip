@@ -348,7 +348,7 @@ void prefill_kernel(PrefillArgs a) {
     // lane's tile base + lane: block id -> the tile's index in the cache (once per window)
     auto tile_offset = [&](int blk, int base) -> int {
         blk = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
-        return (blk * a.num_kv_heads + h) * tpb + (base + lane) % tpb;
+        return (blk * tpb + (base + lane) % tpb) * a.num_kv_heads + h;
     };
     const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
     const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
