@@ -8,43 +8,110 @@ namespace pkv {
 namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kWaveSize = 64;
 
-// One workgroup per (token, kv head); one thread per head-dim position.
-// Writing new tokens into the slots of their blocks is the "scatter" half of
-// paged KV access (ksqn.cn "大模型推理性能优化：PagedAttention与Continuous
-// Batching原理与实践", section 2.2).  Thread d stores V element d; threads with
-// d % X == 0 also copy the 16-byte K group of dims d .. d+X-1.
+// Lane `lane`'s 64-bit value; the low half is taken unsigned, so offsets of 2^31
+// elements and more (caches over 4 GiB of bf16) keep their value.
+__device__ __forceinline__ long long readlane_i64(long long x, int lane) {
+    const unsigned lo = static_cast<unsigned>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<unsigned long long>(x)), lane));
+    const unsigned hi = static_cast<unsigned>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<unsigned long long>(x) >> 32), lane));
+    return static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// Writing new tokens into the slots of their blocks is the "scatter" half of paged
+// KV access (ksqn.cn "大模型推理性能优化：PagedAttention与Continuous Batching原理与实践",
+// section 2.2).  One wavefront per (window of 16 consecutive tokens, kv head).
+//
+// A V 16-byte group holds four consecutive slots (4j .. 4j+3 of a tile) of E dims,
+// so a single token can only write 2- or 4-byte pieces of it.  Tokens k .. k+3 of
+// the window whose slots are s .. s+3 with s a multiple of 4 (a prompt chunk's
+// tokens get consecutive slots, wherever the chunk starts in the batch) fill whole
+// groups: the window's V rows are staged in LDS and each such quad's groups are
+// stored as 16-byte writes.  Tokens in no such quad are written element by
+// element.  K groups hold one token each and are always 16-byte writes.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void reshape_and_cache_kernel(
+__global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const int64_t* __restrict__ slots,
-    T* __restrict__ k_cache, T* __restrict__ v_cache, int num_kv_heads, int block_size,
-    int64_t num_slots) {
+    int num_tokens, T* __restrict__ k_cache, T* __restrict__ v_cache, int num_kv_heads,
+    int block_size, int64_t num_slots) {
     constexpr int X = 16 / sizeof(T);  // elements per 16-byte group
     constexpr int E = X / 4;           // dims per 16-byte V group
-    const int t = blockIdx.x;
+    constexpr int KG = D / X;          // 16-byte K groups per token (also per V row)
+    constexpr int TW = 16;             // tokens per window
+    __shared__ __attribute__((aligned(16))) T vrow[TW][D];
+    const int t0 = TW * static_cast<int>(blockIdx.x);
     const int h = blockIdx.y;
-    const int d = threadIdx.x;
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) return;
-    const int64_t b = slot / block_size;
-    const int o = static_cast<int>(slot - b * block_size);
+    const int lane = threadIdx.x;
     const int tpb = block_size / kTile;
-    const size_t tile_base =
-        ((static_cast<size_t>(b) * tpb + (o >> 4)) * num_kv_heads + h) * (kTile * D);
-    const size_t src = (static_cast<size_t>(t) * num_kv_heads + h) * D;
-    const int ti = o & 15;
-    // V: 16-byte group (m, j, i) holds tokens 4j..4j+3 of dims 16E*m + 16e + i.
-    const int m = d / (16 * E);
-    const int e = (d >> 4) % E;
-    const int i = d & 15;
-    const int j = ti >> 2;
-    const int r = ti & 3;
-    v_cache[tile_base + ((((m * 4 + j) * 16 + i) * E + e) * 4 + r)] = v[src + d];
-    // K: 16-byte group (c, token) holds dims c*X .. c*X+X-1 of one token.
-    if (d % X == 0) {
-        const int c = d / X;
-        *reinterpret_cast<u32x4*>(k_cache + tile_base + (c * 16 + ti) * X) =
-            *reinterpret_cast<const u32x4*>(k + src + d);
+    const int bshift = __builtin_ctz(static_cast<unsigned>(block_size));  // a power of two
+    // lane k < 16: token t0 + k's slot (-1 = skip), its tile's element offset and slot in tile
+    long long my = -1;
+    if (lane < TW && t0 + lane < num_tokens) {
+        const int64_t sv = slots[t0 + lane];
+        my = (sv >= 0 && sv < num_slots) ? sv : -1;
+    }
+    long long tb = 0;
+    int ti = 0;
+    if (my >= 0) {
+        const long long b = my >> bshift;
+        const int o = static_cast<int>(my & (block_size - 1));
+        tb = ((b * tpb + (o >> 4)) * num_kv_heads + h) * static_cast<long long>(kTile * D);
+        ti = o & 15;
+    }
+    const long long n1 = __shfl_down(my, 1), n2 = __shfl_down(my, 2), n3 = __shfl_down(my, 3);
+    const bool qstart = lane < TW - 3 && my >= 0 && (my & 3) == 0 && n1 == my + 1 &&
+                        n2 == my + 2 && n3 == my + 3;
+    const uint32_t qmask = static_cast<uint32_t>(__ballot(qstart));
+    const uint32_t valid = static_cast<uint32_t>(__ballot(my >= 0)) & 0xffffu;
+    const uint32_t covered = (qmask | (qmask << 1) | (qmask << 2) | (qmask << 3)) & 0xffffu;
+    // K of every token, and V rows into LDS: lane covers (token r, 16-byte chunk c)
+    for (int g = lane; g < TW * KG; g += kWaveSize) {
+        const int r = g / KG, c = g % KG;
+        const long long tbr = __shfl(tb, r);
+        const int tir = __shfl(ti, r);
+        if (!((valid >> r) & 1u)) continue;
+        const size_t src = (static_cast<size_t>(t0 + r) * num_kv_heads + h) * D + c * X;
+        *reinterpret_cast<u32x4*>(k_cache + tbr + (c * 16 + tir) * X) =
+            *reinterpret_cast<const u32x4*>(k + src);
+        *reinterpret_cast<u32x4*>(&vrow[r][c * X]) = *reinterpret_cast<const u32x4*>(v + src);
+    }
+    __syncthreads();
+    // V of each quad: group (m, j, i) holds dims 16E*m + 16e + i (e < E) of its 4 tokens
+    for (uint32_t qm = qmask; qm != 0; qm &= qm - 1) {
+        const int q = __builtin_ctz(qm);
+        const long long tbq = readlane_i64(tb, q);
+        const int j = __builtin_amdgcn_readlane(ti, q) >> 2;
+        for (int g = lane; g < D / E; g += kWaveSize) {
+            const int m = g / 16, i = g % 16;
+            u32x4 w;
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int d = 16 * E * m + 16 * e + i;
+                        w[2 * e + h2] = static_cast<uint32_t>(vrow[q + 2 * h2][d]) |
+                                        (static_cast<uint32_t>(vrow[q + 2 * h2 + 1][d]) << 16);
+                    }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[r] = static_cast<uint32_t>(vrow[q + r][16 * m + i]);
+            }
+            *reinterpret_cast<u32x4*>(v_cache + tbq + (((m * 4 + j) * 16 + i) * E) * 4) = w;
+        }
+    }
+    // V of the tokens in no quad, element by element
+    for (uint32_t um = valid & ~covered; um != 0; um &= um - 1) {
+        const int r = __builtin_ctz(um);
+        const long long tbr = readlane_i64(tb, r);
+        const int tir = __builtin_amdgcn_readlane(ti, r);
+        const int j = tir >> 2, rr = tir & 3;
+        for (int d = lane; d < D; d += kWaveSize) {
+            const int m = d / (16 * E), e = (d >> 4) % E, i = d & 15;
+            v_cache[tbr + ((((m * 4 + j) * 16 + i) * E + e) * 4 + rr)] = vrow[r][d];
+        }
     }
 }
 
@@ -212,9 +279,9 @@ hipError_t launch_append(const void* k, const void* v, const int64_t* slots, con
 template <typename T, int D>
 hipError_t launch_rc(const void* k, const void* v, const int64_t* slots, int num_tokens,
                      void* kc, void* vc, int hkv, int bs, int nb, hipStream_t st) {
-    dim3 grid(num_tokens, hkv);
-    hipLaunchKernelGGL((reshape_and_cache_kernel<T, D>), grid, dim3(D), 0, st,
-                       static_cast<const T*>(k), static_cast<const T*>(v), slots,
+    dim3 grid((num_tokens + 15) / 16, hkv);
+    hipLaunchKernelGGL((reshape_and_cache_kernel<T, D>), grid, dim3(kWaveSize), 0, st,
+                       static_cast<const T*>(k), static_cast<const T*>(v), slots, num_tokens,
                        static_cast<T*>(kc), static_cast<T*>(vc), hkv, bs,
                        static_cast<int64_t>(nb) * bs);
     return hipGetLastError();
