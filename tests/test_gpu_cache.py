@@ -44,6 +44,77 @@ def test_reshape_and_cache_bitexact(dtype, D, B):
     assert np.array_equal(to_storage(vd), vc)
 
 
+def _prompt_runs(rng, num_slots, lengths):
+    """Disjoint runs of consecutive slots (prompt chunks), starting anywhere, in shuffled order."""
+    runs, pos = [], 0
+    for L in lengths:
+        pos += int(rng.integers(0, 8))
+        assert pos + L <= num_slots
+        runs.append(np.arange(pos, pos + L, dtype=np.int64))
+        pos += L
+    order = rng.permutation(len(runs))
+    return np.concatenate([runs[i] for i in order])
+
+
+@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 16), ("bf16", 64, 32), ("f32", 128, 16),
+                                       ("f32", 64, 64)])
+def test_reshape_and_cache_prompt_runs_bitexact(dtype, D, B):
+    """Chunks of consecutive slots whose lengths and starts are not multiples of 4, so
+    the kernel's four-slot groups begin at every offset of its 16-token windows, mixed
+    with skipped (-1) and scattered slots."""
+    nb, H = 64, 2
+    spec = ops.CacheSpec(num_blocks=nb, block_size=B, num_kv_heads=H, head_dim=D, dtype=dtype)
+    lay = CacheLayout(nb, H, B, D, dtype)
+    kc, vc = _random_pool(spec, 5)
+    rng = gen.stream(6, 52)
+    runs = _prompt_runs(rng, nb * B - 64, [5, 7, 13, 16, 3, 31, 1, 40, 22, 9, 4, 18])
+    used = set(runs.tolist())
+    free = np.array([x for x in range(nb * B) if x not in used], dtype=np.int64)
+    singles = rng.choice(free, 6, replace=False)
+    slots = np.concatenate([runs[:50], [-1, -1], singles[:3], runs[50:], singles[3:], [-1]])
+    T = len(slots)
+    k = gen.draw_values(rng, (T, H, D), dtype)
+    v = gen.draw_values(rng, (T, H, D), dtype)
+    kd, vd = to_device(kc, spec), to_device(vc, spec)
+    ops.reshape_and_cache(spec, to_device(k, spec), to_device(v, spec),
+                          torch.from_numpy(slots).cuda(), kd, vd)
+    torch.cuda.synchronize()
+    oracle_reshape_and_cache(lay, k, v, slots, kc, vc)
+    assert np.array_equal(to_storage(kd), kc)
+    assert np.array_equal(to_storage(vd), vc)
+
+
+def test_reshape_and_cache_past_2_31_elements():
+    """A pool of more than 2^31 elements per cache array (4.6 GB of bf16 each): tokens
+    written into its last blocks, as whole four-slot groups and one by one, land
+    exactly where the oracle puts them; the block before them is untouched.  Element
+    offsets past 2^31 must survive the kernel's 64-bit offset arithmetic."""
+    nb, H, B, D = 140_000, 8, 16, 128
+    spec = ops.CacheSpec(num_blocks=nb, block_size=B, num_kv_heads=H, head_dim=D, dtype="bf16")
+    per_block = H * B * D
+    assert (nb - 8) * per_block > 2 ** 31
+    kd = torch.zeros(spec.elems, dtype=torch.bfloat16, device="cuda")
+    vd = torch.zeros(spec.elems, dtype=torch.bfloat16, device="cuda")
+    base = nb - 8                                       # the last 8 blocks
+    rng = gen.stream(7, 53)
+    run = np.arange(base * B + 3, base * B + 3 + 37, dtype=np.int64)  # starts mid-quad
+    singles = np.array([(nb - 1) * B + 15, (nb - 2) * B + 6], dtype=np.int64)
+    slots = np.concatenate([run, singles])
+    T = len(slots)
+    k = gen.draw_values(rng, (T, H, D), "bf16")
+    v = gen.draw_values(rng, (T, H, D), "bf16")
+    ops.reshape_and_cache(spec, to_device(k, spec), to_device(v, spec),
+                          torch.from_numpy(slots).cuda(), kd.view(-1), vd.view(-1))
+    torch.cuda.synchronize()
+    lay = CacheLayout(8, H, B, D, "bf16")
+    kc, vc = lay.empty_cache(), lay.empty_cache()
+    oracle_reshape_and_cache(lay, k, v, slots - base * B, kc, vc)
+    lo = base * per_block
+    assert np.array_equal(to_storage(kd[lo:]), kc)
+    assert np.array_equal(to_storage(vd[lo:]), vc)
+    assert not kd[lo - per_block:lo].any() and not vd[lo - per_block:lo].any()
+
+
 def test_reshape_and_cache_skips_out_of_range_slots():
     spec = ops.CacheSpec(num_blocks=4, block_size=16, num_kv_heads=2, head_dim=64, dtype="bf16")
     kc, vc = _random_pool(spec, 3)
