@@ -209,6 +209,16 @@ def test_full_size_config_sampled(name):
     ref = b.expected(pick)
     assert_close(to_float64(out[pick], spec.dtype), ref, spec.dtype, f"{name} sampled {pick}")
     assert np.isfinite(to_float64(out, spec.dtype)).all()
+    # every sequence, merged in the kernel, equals the two-kernel path bit for bit
+    units = ops.default_units()
+    ws = ops.decode_workspace(spec, cfg.num_q_heads, units)
+    two = torch.full((b.S, cfg.num_q_heads, cfg.head_dim), float("nan"), dtype=spec.torch_dtype,
+                     device="cuda")
+    args = (spec, two, b.q, b.cache.k, b.cache.v, b.tables, b.ctx_dev, cfg.scale, units, ws)
+    ops.paged_attn_decode_partial(*args)
+    ops.paged_attn_decode_merge(*args)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_storage(two).view(np.uint8), out.view(np.uint8))
 
 
 # ----------------------------------------------------------------------------- two calls vs one
