@@ -900,6 +900,7 @@ def main():
         if st != 0 or done != S:
             raise RuntimeError(f"append_batch failed at step {n}: status {st}")
         ctx_now[:] += 1
+        ha = time.perf_counter()
         # a2: the step's metadata into a pinned ring slot the write kernel reads in place
         r = n % R
         if ring_ev[r] is not None:
@@ -907,6 +908,7 @@ def main():
             # wake-up leaves the GPU without work
             while not ring_ev[r].query():
                 pass
+        hw = time.perf_counter()
         ps, pc, pu, pp = (x.numpy() for x in views(pin[r]))
         ps[:] = slots
         pc[:] = ctx_now
@@ -938,7 +940,8 @@ def main():
         ring_ev[r] = e2  # the ring slot is free again once the step's launches are done
         if mode == "timed":
             step_tok.append(int(ctx_now.sum()))
-            host.append((h1 - h0, time.perf_counter() - h0))
+            # (allocator, waiting for the ring slot, staging the metadata, whole host side)
+            host.append((ha - h0, hw - ha, h1 - hw, time.perf_counter() - h0))
 
     ev = {"timed": [], "profile": []}
     step_tok = []  # sum of context lengths of every timed step
@@ -1057,8 +1060,13 @@ def main():
                                              / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
                  if Hq > Hkv and cfg.dtype == "bf16" else None),
         "host_bookkeeping_us_median": round(float(np.median([h[0] for h in host])) * 1e6, 2),
-        "host_step_us_median": round(float(np.median([h[1] for h in host])) * 1e6, 2),
-        "host_step_us_max": round(float(np.max([h[1] for h in host])) * 1e6, 2),
+        "host_staging_us_median": round(float(np.median([h[2] for h in host])) * 1e6, 2),
+        "host_ring_wait_us_median": round(float(np.median([h[1] for h in host])) * 1e6, 2),
+        "host_step_us_median": round(float(np.median([h[3] for h in host])) * 1e6, 2),
+        "host_step_us_max": round(float(np.max([h[3] for h in host])) * 1e6, 2),
+        "host_note": "bookkeeping = the library allocator reserving every sequence's next slot; "
+                     "staging = writing the step's metadata into its pinned ring slot; ring wait = "
+                     "waiting for the GPU to free that slot (the host runs ahead of the GPU)",
         "roofline": {
             "kernel": "decode_pass1 (gather + attention, merge of split sequences folded in)",
             "bound": "hbm",
