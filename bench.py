@@ -498,10 +498,11 @@ def run_tiny(args):
     tables, ctx_dev, _, ctx_h = cache.metadata(range(S))
     q = to_device(gen.q_values(cfg.seed, 1, S, Hq, D, cfg.dtype), spec)
     out = torch.empty(S, Hq, D, dtype=spec.torch_dtype, device="cuda")
-    ws = ops.decode_workspace(spec, Hq, 0)
+    units = args.units if args.units > 0 else 0
+    ws = ops.decode_workspace(spec, Hq, units)
     stream = torch.cuda.current_stream()
     write = ops.bind_reshape_and_cache(spec, k_new, v_new, slots_dev, cache.k, cache.v, stream)
-    decode = ops.bind_decode(spec, out, q, cache.k, cache.v, tables, ctx_dev, cfg.scale, 0, ws)
+    decode = ops.bind_decode(spec, out, q, cache.k, cache.v, tables, ctx_dev, cfg.scale, units, ws)
     for _ in range(args.warmup):
         write()
         decode()
@@ -540,7 +541,8 @@ def run_tiny(args):
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.title}", "seqs": S, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": D, "block_size": B, "pool_blocks": cfg.num_blocks,
-                   "context_lens": [int(x) for x in ctx_h], "seed": cfg.seed},
+                   "context_lens": [int(x) for x in ctx_h], "seed": cfg.seed,
+                   "units": units or "library default"},
         "write_us": {"median": round(float(np.median(t_w)) * 1e6, 2), "min": round(float(np.min(t_w)) * 1e6, 2)},
         "decode_us": {"median": round(float(np.median(t_d)) * 1e6, 2), "min": round(float(np.min(t_d)) * 1e6, 2)},
         "kv_bytes_per_step": kv_bytes,
