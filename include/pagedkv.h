@@ -209,7 +209,11 @@ pa_status pa_paged_attn_decode(const pa_cache_desc* desc, void* out, const void*
 
 /*
  * pa_paged_attn_decode enqueues one kernel.  It gathers and attends: each wave
- * takes an equal range of the batch's 16-token tiles, writes the sequences it
+ * takes a range of 16-token tiles.  A row is a kv head (bf16 with G > 1) or a
+ * query head (otherwise).  With num_units >= rows every row is cut into the
+ * same num_units / rows ranges, of equal cost where a sequence costs its tile
+ * count plus one; with fewer units the batch's tiles, row after row, are cut
+ * into num_units ranges of equal tile count.  A wave writes the sequences it
  * holds whole to `out` and leaves partial (max, sum, accumulator) records for
  * sequences cut by range ends.  The holder of a cut sequence's pieces that
  * finishes last (found with the workspace's arrival counts) merges the records

@@ -1,5 +1,6 @@
 // Paged decode attention for gfx950: pass 1 (block-table gather, QK^T, online
-// softmax, PV) and pass 2 (log-sum-exp merge of split sequences).
+// softmax, PV) and the log-sum-exp merge of split sequences, either inside pass 1
+// (the default, one kernel) or as a separate pass 2.
 //
 // What is computed: one new query token per sequence attends over every cached
 // token of its sequence (ksqn.cn "大模型推理性能优化：PagedAttention与Continuous
@@ -22,7 +23,10 @@
 // of one workgroup and meet once per tile, so the adjacent 4 KiB head slices of
 // a block are requested together.  A sequence that a range holds whole is
 // finished in place; a sequence cut by range ends leaves partial (max, sum,
-// accumulator) records, and pass 2 merges them with the log-sum-exp rule.
+// accumulator) records.  In the single-kernel form each holder then adds one to
+// an arrival count kept for the sequence's last holder; the holder whose add
+// completes it merges the records with the log-sum-exp rule and resets the
+// count.  In the two-kernel form pass 2 does the same merge, in the same order.
 // Every wave scans the context lengths itself to find its range, so no
 // planning kernel runs first.
 //
