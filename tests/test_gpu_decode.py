@@ -129,6 +129,22 @@ def test_poisoned_padding_columns_change_nothing():
     assert np.array_equal(base, poisoned)
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 16, 4), ("bf16", 8, 8), ("f32", 4, 2)])
+@pytest.mark.parametrize("units", [0, 3, 40])
+def test_context_lengths_outside_the_table_are_clamped(dtype, Hq, Hkv, units):
+    """Lengths past what a table row addresses (max_blocks_per_seq * B) act as that
+    maximum and negative ones as zero: the output equals, bit for bit, the call with
+    the clamped lengths, and the oracle on them."""
+    true_ctx = [48, 16, 48, 0, 5, 47]
+    spec = ops.CacheSpec(num_blocks=64, block_size=16, num_kv_heads=Hkv, head_dim=128, dtype=dtype)
+    b = Batch(spec, true_ctx, Hq, seed=33, free_order=gen.pool_permutation(8, 64), max_blocks=3)
+    wild = torch.tensor([49, 16, 2**31 - 1, -7, 5, 47], dtype=torch.int32, device="cuda")
+    got = b.run(num_units=units, ctx=wild)
+    assert np.array_equal(got.view(np.uint8), b.run(num_units=units).view(np.uint8))
+    assert_close(to_float64(got, dtype), b.expected(), dtype, f"clamped lengths, units {units}")
+    assert not to_float64(got[3], dtype).any()
+
+
 @pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 32, 8), ("bf16", 8, 8)])
 def test_unit_count_sweep(dtype, Hq, Hkv):
     """Every split of the work (one unit .. more units than tiles) stays within tolerance."""
