@@ -116,6 +116,22 @@ def test_chunk_longer_than_cache_gives_zero_rows():
     assert_close(out[3:8], ref, "bf16", "valid rows")
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4)])
+def test_cache_lengths_past_the_table_are_clamped(Hq, Hkv):
+    """Cache lengths past what a table row addresses (max_blocks_per_seq * B) act as
+    that maximum: rows equal, bit for bit, the call with the true lengths, and the
+    oracle on them."""
+    spec = ops.CacheSpec(num_blocks=32, block_size=16, num_kv_heads=Hkv, head_dim=128, dtype="bf16")
+    b = Chunks(spec, [(48, 10), (48, 48), (20, 5)], Hq, seed=47,
+               free_order=gen.pool_permutation(47, 32))
+    assert b.tables.shape[1] == 3
+    wild = b.run(L=[53, 2**31 - 1, 20])
+    assert np.array_equal(wild.view(np.uint8), b.run().view(np.uint8))
+    out = to_f64(wild, "bf16")
+    for s in range(b.S):
+        assert_close(out[b.qs[s]:b.qs[s + 1]], b.expected(s), "bf16", f"seq {s}")
+
+
 def test_single_token_chunks_match_decode():
     """A one-token chunk is a decode step: compare with the decode kernel and the oracle."""
     spec = ops.CacheSpec(num_blocks=400, block_size=16, num_kv_heads=8, head_dim=128, dtype="bf16")
