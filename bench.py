@@ -18,6 +18,7 @@ and the CPU oracle timed on a sample of the same batch.
 from __future__ import annotations
 
 import argparse
+import collections
 import gc
 import json
 import math
@@ -861,10 +862,14 @@ def main():
     # A ring of pinned host buffers holds each step's metadata; the cache-write
     # kernel reads it in place (no separate host-to-device copy) and forwards the
     # context lengths to the device array the decode kernels read.
-    R = 4
+    # Slot n % R is reused by step n + R, once step n's launches are done.  An event
+    # recorded on the stream is a marker packet that holds the next launch back by
+    # ~6 us, so one is recorded only every EV_EVERY steps (and on the sampled timed
+    # steps); a later step's event also covers the earlier steps.
+    R, EV_EVERY = 8, 4
     words = S * 2 + S + 3 * S + 2 * S  # int32 words: slots (int64), ctx, updates, cow pairs
     pin = [torch.empty(words, dtype=torch.int32, pin_memory=True) for _ in range(R)]
-    ring_ev = [None] * R
+    ring_ev = collections.deque()  # (step, event), oldest first
     ctx_dev = torch.from_numpy(ctx0.astype(np.int32)).cuda()
 
     def views(buf):
@@ -894,7 +899,7 @@ def main():
         """mode "warm": no timing events; "timed": events around the decode kernel
         (the kernel the roofline is taken on) on every 5th step; "profile": events
         around every launch.  A marker between the write and the decode launch delays
-        the decode (measured: 2.3 us per step), so the other steps record only the
+        the decode (measured: 2.3 us per step), so the other steps record at most the
         ring-slot event, after the decode."""
         h0 = time.perf_counter()
         # a1: host bookkeeping in the library allocator
@@ -905,10 +910,13 @@ def main():
         ha = time.perf_counter()
         # a2: the step's metadata into a pinned ring slot the write kernel reads in place
         r = n % R
-        if ring_ev[r] is not None:
-            # poll rather than block: a blocking wait may sleep the thread, and a late
-            # wake-up leaves the GPU without work
-            while not ring_ev[r].query():
+        if n >= R:
+            while ring_ev[0][0] < n - R:
+                ring_ev.popleft()  # older than the slot's last user: covers nothing needed
+            # the first event at or after step n - R (one is recorded at least every
+            # EV_EVERY <= R steps); poll rather than block: a blocking wait may sleep
+            # the thread, and a late wake-up leaves the GPU without work
+            while not ring_ev[0][1].query():
                 pass
         hw = time.perf_counter()
         ps, pc, pu, pp = (x.numpy() for x in views(pin[r]))
@@ -936,10 +944,13 @@ def main():
         if timing:
             e2.record(stream)
             ev[mode].append((e0, e1, e2, int(ctx_now.sum())))
-        else:
+        elif n % EV_EVERY == EV_EVERY - 1:
             e2 = torch.cuda.Event()
             e2.record(stream)
-        ring_ev[r] = e2  # the ring slot is free again once the step's launches are done
+        else:
+            e2 = None
+        if e2 is not None:
+            ring_ev.append((n, e2))  # slots of steps <= n are free once e2 has completed
         if mode == "timed":
             step_tok.append(int(ctx_now.sum()))
             # (allocator, waiting for the ring slot, staging the metadata, whole host side)
