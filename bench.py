@@ -272,8 +272,9 @@ def run_trace(args):
         if d["S"]:
             ops.append_tokens(spec, d["k"], d["v"], d["dslots"], kc, vc, cow_pairs=d["cows"])
             e1.record(stream)
+            # prefix-cached prompts share blocks between sequences: keep them cached
             ops.paged_attn_decode(spec, d["out"], d["q"], kc, vc, d["tables"], d["ctx"], cfg.scale,
-                                  units, ws)
+                                  units, ws, keep_cached=bool(cfg.prefix))
         else:
             e1.record(stream)
         e2.record(stream)
@@ -885,6 +886,9 @@ def main():
     # Every launch of every step is bound once (arguments converted up front); the
     # per-step metadata has a fixed shape (a copy-on-write row and a table-update row
     # per sequence, -1 when there is none), so a step's launches never change form.
+    # Sequences forked from one parent share its blocks: those are read with ordinary
+    # loads so that the shared prefix stays cached; private contexts are streamed.
+    shared = cfg.ctx_kind == "shared_prefix"
     calls = []
     for n in range(total_steps):
         hs, hc, hu, hp = views(pin[n % R])
@@ -893,7 +897,7 @@ def main():
                                    block_tables=tables, table_updates=hu, lens_in=hc,
                                    lens_out=ctx_dev),
             ops.bind_decode(spec, out, qs[n], cache.k, cache.v, tables, ctx_dev, cfg.scale, units,
-                            ws)))
+                            ws, keep_cached=shared)))
 
     def step(n, mode):
         """mode "warm": no timing events; "timed": events around the decode kernel
@@ -1046,7 +1050,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.title}", "seqs": S, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": D, "block_size": B, "pool_blocks": cfg.num_blocks,
-                   "sum_ctx_first_step": int(tok[0]), "units": units, "seed": cfg.seed},
+                   "sum_ctx_first_step": int(tok[0]), "units": units, "seed": cfg.seed,
+                   "kv_loads": "cached (shared blocks)" if shared else "streamed (non-temporal)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "shared_prefix_unique": unique,
         "us_per_step": round(wall / steps * 1e6, 2),

@@ -158,6 +158,17 @@ pa_status pa_append_tokens(const pa_cache_desc* desc, const void* k, const void*
                            const int32_t* lens_in, int32_t* lens_out, int32_t num_lens,
                            void* stream);
 
+/* Decode flags (the `flags` argument of the pa_paged_attn_decode calls). */
+enum {
+    /* Read K/V tiles with ordinary loads, which keep them in L2 and the
+     * last-level cache.  Set it when blocks are shared between the batch's
+     * sequences (a forked or prefix-cached prompt), so that a shared block is
+     * read from HBM once per call.  Without it tiles are read with
+     * non-temporal loads, which do not displace cached data and stream a
+     * batch of private contexts faster. */
+    PA_DECODE_KEEP_CACHED = 1
+};
+
 /*
  * Decode attention.
  *
@@ -180,6 +191,8 @@ pa_status pa_append_tokens(const pa_cache_desc* desc, const void* k, const void*
  *                  The split decides the order of floating-point reductions,
  *                  so results are bit-reproducible for a given
  *                  (context_lens, num_units) and independent of block IDs.
+ *   flags          0 or PA_DECODE_KEEP_CACHED; other bits give
+ *                  PA_ERR_INVALID_ARG.  Results do not depend on it.
  *   workspace      device scratch of at least pa_decode_workspace_bytes()
  *                  bytes, 16-B aligned, owned by the caller.  It holds partial
  *                  results and, in its last 4 * num_units bytes, one arrival
@@ -205,7 +218,8 @@ pa_status pa_paged_attn_decode(const pa_cache_desc* desc, void* out, const void*
                                const int32_t* block_tables, const int32_t* context_lens,
                                int32_t num_seqs, int32_t num_q_heads,
                                int32_t max_blocks_per_seq, float scale, int32_t num_units,
-                               void* workspace, size_t workspace_bytes, void* stream);
+                               void* workspace, size_t workspace_bytes, uint32_t flags,
+                               void* stream);
 
 /*
  * pa_paged_attn_decode enqueues one kernel.  It gathers and attends: each wave
@@ -231,13 +245,13 @@ pa_status pa_paged_attn_decode_partial(const pa_cache_desc* desc, void* out, con
                                        int32_t num_seqs, int32_t num_q_heads,
                                        int32_t max_blocks_per_seq, float scale,
                                        int32_t num_units, void* workspace,
-                                       size_t workspace_bytes, void* stream);
+                                       size_t workspace_bytes, uint32_t flags, void* stream);
 pa_status pa_paged_attn_decode_merge(const pa_cache_desc* desc, void* out, const void* q,
                                      const void* k_cache, const void* v_cache,
                                      const int32_t* block_tables, const int32_t* context_lens,
                                      int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_blocks_per_seq, float scale, int32_t num_units,
-                                     void* workspace, size_t workspace_bytes, void* stream);
+                                     void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
  * Chunked-prefill attention over the paged cache.

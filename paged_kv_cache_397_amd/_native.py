@@ -15,6 +15,7 @@ LIB_PATH = os.environ.get("PAGEDKV_LIBRARY") or os.path.join(
 
 c_i32, c_i64, c_sz, c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 c_vp = ctypes.c_void_p
+c_u32 = ctypes.c_uint32
 P_i32, P_i64 = ctypes.POINTER(c_i32), ctypes.POINTER(c_i64)
 
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM",
@@ -48,11 +49,11 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (c_sz, [P_desc, c_i32, c_i32]),
     "pa_decode_default_units": (c_i32, []),
     "pa_paged_attn_decode": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
-                                     c_i32, c_f32, c_i32, c_vp, c_sz, c_vp]),
+                                     c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_vp]),
     "pa_paged_attn_decode_partial": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
-                                             c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_vp]),
+                                             c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_vp]),
     "pa_paged_attn_decode_merge": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
-                                           c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_vp]),
+                                           c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_vp]),
     "pa_paged_attn_prefill": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                       c_i32, c_i32, c_i32, c_i32, c_f32, c_vp]),
     "pa_alloc_create": (c_i32, [c_i32, c_i32, c_vp, ctypes.POINTER(c_vp)]),

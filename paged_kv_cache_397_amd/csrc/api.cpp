@@ -219,9 +219,10 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
                       const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                       int32_t max_blocks_per_seq, float scale, int32_t num_units, void* workspace,
-                      size_t workspace_bytes, void* stream, int passes) {
+                      size_t workspace_bytes, uint32_t flags, void* stream, int passes) {
     pa_status st = check_desc(d);
     if (st != PA_OK) return st;
+    if ((flags & ~static_cast<uint32_t>(PA_DECODE_KEEP_CACHED)) != 0) return PA_ERR_INVALID_ARG;
     if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || num_units < 0 ||
         num_units > kMaxUnits)
         return PA_ERR_INVALID_ARG;
@@ -277,6 +278,7 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     // ranges, and the rows of a range (up to 8, a power of two dividing the row
     // count) share a workgroup.
     a.fused = passes == 3 ? 1 : 0;
+    a.keep_cached = (flags & PA_DECODE_KEEP_CACHED) ? 1 : 0;
 
     a.aligned = units >= rows ? 1 : 0;
     a.waves_per_group = 1;
@@ -296,10 +298,11 @@ pa_status pa_paged_attn_decode(const pa_cache_desc* d, void* out, const void* q,
                                const int32_t* block_tables, const int32_t* context_lens,
                                int32_t num_seqs, int32_t num_q_heads,
                                int32_t max_blocks_per_seq, float scale, int32_t num_units,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               void* workspace, size_t workspace_bytes, uint32_t flags,
+                               void* stream) {
     return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                        num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
-                       workspace_bytes, stream, 3);
+                       workspace_bytes, flags, stream, 3);
 }
 
 pa_status pa_paged_attn_decode_partial(const pa_cache_desc* d, void* out, const void* q,
@@ -308,10 +311,10 @@ pa_status pa_paged_attn_decode_partial(const pa_cache_desc* d, void* out, const 
                                        int32_t num_seqs, int32_t num_q_heads,
                                        int32_t max_blocks_per_seq, float scale,
                                        int32_t num_units, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+                                       size_t workspace_bytes, uint32_t flags, void* stream) {
     return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                        num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
-                       workspace_bytes, stream, 1);
+                       workspace_bytes, flags, stream, 1);
 }
 
 pa_status pa_paged_attn_decode_merge(const pa_cache_desc* d, void* out, const void* q,
@@ -319,10 +322,11 @@ pa_status pa_paged_attn_decode_merge(const pa_cache_desc* d, void* out, const vo
                                      const int32_t* block_tables, const int32_t* context_lens,
                                      int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_blocks_per_seq, float scale, int32_t num_units,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+                                     void* workspace, size_t workspace_bytes, uint32_t flags,
+                                     void* stream) {
     return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                        num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
-                       workspace_bytes, stream, 2);
+                       workspace_bytes, flags, stream, 2);
 }
 
 pa_status pa_paged_attn_prefill(const pa_cache_desc* d, void* out, const void* q,

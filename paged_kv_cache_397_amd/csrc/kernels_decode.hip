@@ -612,7 +612,10 @@ __device__ __forceinline__ Chunk build_chunk(const DecodeArgs& a, Cursor c, int 
 // Pass 1: one wavefront per unit, NW units (rows of one range) per workgroup.
 // The loop keeps the next tile's K/V loads (and, when that tile opens a new
 // piece, the new query) in flight while the current tile is folded in.
-template <class Path, typename T, int D, int NW>
+// Stream: K/V tiles read with non-temporal loads (a template parameter, not a
+// runtime branch: the compiler would merge two loads of one address and drop the
+// hint).
+template <class Path, typename T, int D, int NW, bool Stream>
 __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     constexpr int NL = Path::NL;
     const int lane = threadIdx.x & (kWave - 1);
@@ -816,13 +819,24 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         f_seq = b.r.seq;
         f_row = b.r.row;
         // Uniform tile base (scalar registers) + lane offset: one contiguous KiB per load.
+        // A tile of private context is read once per call: non-temporal loads stream it
+        // past the caches instead of filling them with lines nobody reads again.
+        // Blocks shared between sequences are re-read within the call, so the caller
+        // can keep them cached instead (ordinary loads).
         const size_t off = static_cast<size_t>(b.r.toff) * Path::TILE_U4;
         const u32x4* kt = kc + off;
         const u32x4* vt = vc + off;
+        if constexpr (!Stream) {
 #pragma unroll
-        for (int s = 0; s < NL; ++s) b.k[s] = kt[lane + s * kWave];
+            for (int s = 0; s < NL; ++s) b.k[s] = kt[lane + s * kWave];
 #pragma unroll
-        for (int s = 0; s < NL; ++s) b.v[s] = vt[lane + s * kWave];
+            for (int s = 0; s < NL; ++s) b.v[s] = vt[lane + s * kWave];
+        } else {
+#pragma unroll
+            for (int s = 0; s < NL; ++s) b.k[s] = __builtin_nontemporal_load(kt + lane + s * kWave);
+#pragma unroll
+            for (int s = 0; s < NL; ++s) b.v[s] = __builtin_nontemporal_load(vt + lane + s * kWave);
+        }
     };
 
     // ---- compute side: the open piece
@@ -963,18 +977,26 @@ hipError_t launch_pass2(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <class Path, typename T, int D, bool Stream>
+hipError_t launch_pass1(const DecodeArgs& a, int nw, int groups, hipStream_t st) {
+    switch (nw) {
+        case 1: hipLaunchKernelGGL((decode_pass1<Path, T, D, 1, Stream>), dim3(groups), dim3(kWave), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((decode_pass1<Path, T, D, 2, Stream>), dim3(groups), dim3(2 * kWave), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((decode_pass1<Path, T, D, 4, Stream>), dim3(groups), dim3(4 * kWave), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((decode_pass1<Path, T, D, 8, Stream>), dim3(groups), dim3(8 * kWave), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
+}
+
 template <class Path, typename T, int D>
 hipError_t launch_two_pass(const DecodeArgs& a, int passes, hipStream_t st) {
     if (passes & 1) {
         const int nw = a.waves_per_group;
         const int groups = nw > 1 ? (a.num_units / a.rows) * a.rows / nw : a.num_units;
-        switch (nw) {
-            case 1: hipLaunchKernelGGL((decode_pass1<Path, T, D, 1>), dim3(groups), dim3(kWave), 0, st, a); break;
-            case 2: hipLaunchKernelGGL((decode_pass1<Path, T, D, 2>), dim3(groups), dim3(2 * kWave), 0, st, a); break;
-            case 4: hipLaunchKernelGGL((decode_pass1<Path, T, D, 4>), dim3(groups), dim3(4 * kWave), 0, st, a); break;
-            case 8: hipLaunchKernelGGL((decode_pass1<Path, T, D, 8>), dim3(groups), dim3(8 * kWave), 0, st, a); break;
-            default: return hipErrorInvalidValue;
-        }
+        const hipError_t e0 = a.keep_cached ? launch_pass1<Path, T, D, false>(a, nw, groups, st)
+                                            : launch_pass1<Path, T, D, true>(a, nw, groups, st);
+        if (e0 != hipSuccess) return e0;
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

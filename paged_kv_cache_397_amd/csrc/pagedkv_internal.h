@@ -35,6 +35,7 @@ struct DecodeArgs {
     int32_t aligned;            // 1: every row cut into num_units / rows identical ranges
     int32_t waves_per_group;    // rows of one range per workgroup (aligned split only)
     int32_t fused;              // 1: pass 1 merges split sequences itself (no pass 2)
+    int32_t keep_cached;        // 1: K/V tiles read with ordinary loads (kept in L2 / MALL)
     float scale_log2e;          // scale * log2(e): scores are kept in base-2 units
 };
 

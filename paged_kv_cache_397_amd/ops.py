@@ -187,8 +187,11 @@ def decode_workspace(spec: CacheSpec, num_q_heads: int, num_units: int = 0, devi
                        device=device)
 
 
+DECODE_KEEP_CACHED = 1  # PA_DECODE_KEEP_CACHED
+
+
 def _decode(fn: str, spec: CacheSpec, out, q, k_cache, v_cache, block_tables, context_lens,
-            scale, num_units, workspace, stream):
+            scale, num_units, workspace, stream, keep_cached=False):
     S, Hq, D = q.shape
     if D != spec.head_dim or tuple(out.shape) != (S, Hq, D):
         raise ValueError("q and out must be [S, Hq, D]")
@@ -205,37 +208,37 @@ def _decode(fn: str, spec: CacheSpec, out, q, k_cache, v_cache, block_tables, co
         _dev(block_tables, "block_tables", torch.int32),
         _dev(context_lens, "context_lens", torch.int32), S, Hq, block_tables.shape[1],
         float(scale), int(num_units), _dev(workspace, "workspace"), workspace.numel(),
-        _stream(stream))
+        DECODE_KEEP_CACHED if keep_cached else 0, _stream(stream))
     N.check(st, fn)
     return out
 
 
 def paged_attn_decode(spec: CacheSpec, out, q, k_cache, v_cache, block_tables, context_lens,
                       scale: float | None = None, num_units: int = 0, workspace=None,
-                      stream=None):
+                      stream=None, keep_cached: bool = False):
     """out[i, j] = softmax attention of q[i, j] over sequence i's cached tokens."""
     return _decode("pa_paged_attn_decode", spec, out, q, k_cache, v_cache, block_tables,
-                   context_lens, scale, num_units, workspace, stream)
+                   context_lens, scale, num_units, workspace, stream, keep_cached)
 
 
 def paged_attn_decode_partial(spec: CacheSpec, out, q, k_cache, v_cache, block_tables,
                               context_lens, scale: float | None = None, num_units: int = 0,
-                              workspace=None, stream=None):
+                              workspace=None, stream=None, keep_cached: bool = False):
     """First kernel of paged_attn_decode (needs the same workspace in the merge)."""
     if workspace is None:
         raise ValueError("the partial/merge split needs an explicit shared workspace")
     return _decode("pa_paged_attn_decode_partial", spec, out, q, k_cache, v_cache, block_tables,
-                   context_lens, scale, num_units, workspace, stream)
+                   context_lens, scale, num_units, workspace, stream, keep_cached)
 
 
 def paged_attn_decode_merge(spec: CacheSpec, out, q, k_cache, v_cache, block_tables,
                             context_lens, scale: float | None = None, num_units: int = 0,
-                            workspace=None, stream=None):
+                            workspace=None, stream=None, keep_cached: bool = False):
     """Second kernel of paged_attn_decode: merges the partial records of split sequences."""
     if workspace is None:
         raise ValueError("the partial/merge split needs an explicit shared workspace")
     return _decode("pa_paged_attn_decode_merge", spec, out, q, k_cache, v_cache, block_tables,
-                   context_lens, scale, num_units, workspace, stream)
+                   context_lens, scale, num_units, workspace, stream, keep_cached)
 
 
 def paged_attn_prefill(spec: CacheSpec, out, q, k_cache, v_cache, block_tables, query_start,
@@ -314,7 +317,7 @@ def bind_append_tokens(spec: CacheSpec, k, v, slot_mapping, k_cache, v_cache, co
 
 def bind_decode(spec: CacheSpec, out, q, k_cache, v_cache, block_tables, context_lens,
                 scale: float | None, num_units: int, workspace, stage: str = "both",
-                stream=None) -> BoundCall:
+                stream=None, keep_cached: bool = False) -> BoundCall:
     """paged_attn_decode (stage "both"), or its first ("partial") or second ("merge")
     kernel, with its arguments fixed."""
     fn = {"both": "pa_paged_attn_decode", "partial": "pa_paged_attn_decode_partial",
@@ -333,4 +336,4 @@ def bind_decode(spec: CacheSpec, out, q, k_cache, v_cache, block_tables, context
         _dev(block_tables, "block_tables", torch.int32),
         _dev(context_lens, "context_lens", torch.int32), S, Hq, block_tables.shape[1],
         ctypes.c_float(scale), int(num_units), _dev(workspace, "workspace"), workspace.numel(),
-        _stream(stream)), keep=desc)
+        DECODE_KEEP_CACHED if keep_cached else 0, _stream(stream)), keep=desc)

@@ -54,12 +54,12 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 
 def _decode(**kw):
     args = dict(desc=_desc(), out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, ctx=FAKE, S=4, Hq=2,
-                maxB=3, scale=0.125, units=8, ws=FAKE, wsb=1 << 30)
+                maxB=3, scale=0.125, units=8, ws=FAKE, wsb=1 << 30, flags=0)
     args.update(kw)
     return N.lib().pa_paged_attn_decode(ctypes.byref(args["desc"]), args["out"], args["q"],
                                         args["k"], args["v"], args["bt"], args["ctx"], args["S"],
                                         args["Hq"], args["maxB"], args["scale"], args["units"],
-                                        args["ws"], args["wsb"], None)
+                                        args["ws"], args["wsb"], args["flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -70,6 +70,8 @@ def _decode(**kw):
     (dict(units=-2), N.PA_ERR_INVALID_ARG),
     (dict(wsb=16), N.PA_ERR_INVALID_ARG),                # workspace too small
     (dict(scale=float("nan")), N.PA_ERR_INVALID_ARG),
+    (dict(flags=2), N.PA_ERR_INVALID_ARG),               # unknown flag bit
+    (dict(flags=1, out=None), N.PA_ERR_INVALID_ARG),     # PA_DECODE_KEEP_CACHED is accepted
     (dict(maxB=0), N.PA_ERR_INVALID_ARG),
     (dict(desc=_desc(head_dim=256)), N.PA_ERR_UNSUPPORTED),
     (dict(desc=_desc(block_size=48)), N.PA_ERR_UNSUPPORTED),

@@ -198,6 +198,12 @@ def test_shared_prefix_fork_and_copy_on_write():
     for k, s in enumerate(seqs):
         ref = contiguous_decode(q_host[k], *logical[s], 1 / math.sqrt(D), "bf16")
         assert_close(to_float64(got[k], "bf16"), ref, "bf16", f"shared seq {s}")
+    # the load policy for shared blocks changes nothing but where lines are cached
+    kept = torch.empty_like(q)
+    ops.paged_attn_decode(spec, kept, q, cache.k, cache.v, tables, ctx, 1 / math.sqrt(D),
+                          num_units=6, keep_cached=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_storage(kept).view(np.uint8), got.view(np.uint8))
     # private copies of the same logical data
     priv = PagedKVCache(spec, None, fill=float("nan"))
     for s in seqs:
@@ -235,6 +241,12 @@ def test_full_size_config_sampled(name):
     ops.paged_attn_decode_merge(*args)
     torch.cuda.synchronize()
     assert np.array_equal(to_storage(two).view(np.uint8), out.view(np.uint8))
+    # ordinary loads (PA_DECODE_KEEP_CACHED) instead of non-temporal ones: same bits
+    kept = torch.full_like(two, float("nan"))
+    ops.paged_attn_decode(spec, kept, b.q, b.cache.k, b.cache.v, b.tables, b.ctx_dev, cfg.scale,
+                          units, ws, keep_cached=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_storage(kept).view(np.uint8), out.view(np.uint8))
 
 
 # ----------------------------------------------------------------------------- two calls vs one
