@@ -794,8 +794,11 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         if (arrive_first) arrive();
         // The rows of a workgroup walk the same tiles; meeting once per tile keeps
         // their requests for one block's adjacent heads (consecutive 4 KiB pieces of
-        // K and of V) reaching memory together.
-        if constexpr (NW > 1) __syncthreads();
+        // K and of V) reaching memory together.  Measured with streamed loads, that
+        // pays for the per-head path (G = 1: 343 against 352 us on a batch of 64
+        // 32-head sequences) but not for the group path (G = 4: 220 us without it
+        // against 221 with it on a batch of 256), which therefore runs without it.
+        if constexpr (NW > 1 && Path::GH == 1) __syncthreads();
         while (kf == ch.n) {  // chunk used up: describe the next tiles (empty chunks only
                               // arise from runs of sequences with no cached tokens)
             if (ch.next.row >= a.rows) {
