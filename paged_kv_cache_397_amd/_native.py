@@ -9,9 +9,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-# The in-package build; PAGEDKV_LIBRARY may name another build of the same sources.
-LIB_PATH = os.environ.get("PAGEDKV_LIBRARY") or os.path.join(
-    os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# Always the in-package build: no environment variable can point the binding at
+# another copy of the library.
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 c_i32, c_i64, c_sz, c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 c_vp = ctypes.c_void_p

@@ -51,6 +51,22 @@ namespace {
 // Partial records are written and read at device scope (write-through past this
 // XCD's L2, reads from the device-coherent level), so a record written by one
 // XCD can be merged by another in the same launch without cache maintenance.
+//
+// The in-launch merge hands records between workgroups with relaxed device-scope
+// atomics only: a holder's record stores, then `s_waitcnt vmcnt(0)`, then a relaxed
+// fetch-add on the arrival count; the merger reads the records with relaxed
+// device-scope loads after it has seen the count complete.  The language memory
+// model orders none of this (there is no release on the add and no acquire before
+// the reads).  It is correct on gfx950 because (1) device-scope atomic stores are
+// written through to the device-coherent level, (2) on gfx9 the vector-memory
+// counter also counts stores, and waiting it to zero waits for their completion
+// acknowledgement, and (3) device-scope atomic loads are not served from a
+// non-coherent cache.  Agent-scope release/acquire fences would add an L2
+// write-back and invalidate per piece.  The assumption is tied to this ISA, so
+// the file refuses to compile for any other target.
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
+#error "the decode kernels' in-launch merge relies on gfx950 memory behaviour; build for gfx950 only"
+#endif
 __device__ __forceinline__ void store_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
