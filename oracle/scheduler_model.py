@@ -21,7 +21,10 @@ Readings where the pages are silent (the library's scheduler takes the same):
   is read as FCFS because the allocation sample on the same pages is FIFO.
 * Admission allocates blocks for the whole prompt at once; the prompt is then
   written in chunks of at most `chunk` tokens, one chunk per request per step,
-  in admission order.  Prefill attention itself is not modelled.
+  in admission order.  Chunks are planned after the step's decode appends, so a
+  request preempted by an append has no chunk in that step (its blocks may
+  already hold another request's token).  Prefill attention itself is not
+  modelled.
 * A request decodes from the step after its prompt is fully written; each
   decode step appends one token (its slot reserved by the allocator, with a
   new block when the token crosses a block boundary) and attends over every
@@ -38,8 +41,8 @@ Readings where the pages are silent (the library's scheduler takes the same):
   (prefill starts after it), and the first request that does not fit blocks the
   queue as before.  Each prompt chunk's full blocks are registered when the
   chunk is planned (its K/V are written in that step, before any later step can
-  reuse them); after the step's decode appends, every decoding request's newly
-  full blocks are registered, in admission order.  Generated tokens have IDs
+  reuse them); after that, every decoding request's newly full blocks are
+  registered, in admission order.  Generated tokens have IDs
   given by the workload; a preempted request is admitted again with its prompt
   plus the tokens it generated, so its own cached blocks can serve the
   recompute.
@@ -50,8 +53,8 @@ Readings where the pages are silent (the library's scheduler takes the same):
   requests come back first, in swap-out order, each step before any admission;
   while one of them does not fit, no new request is admitted.  A request swapped
   back in rejoins the running list at its end.  The step's device work runs in
-  the order: swap-in copies, prompt writes and prefill, swap-out copies (so that
-  a chunk written this step travels with its request), decode writes and decode.
+  the order: swap-in copies, prompt writes and prefill, swap-out copies, decode
+  writes and decode; a request swapped out in a step has no chunk in it.
 
 Pins: a hand-worked trace on a four-block pool (tests/test_scheduler.py) that
 exercises admission, chunking, release, head-of-line blocking, and preemption
@@ -162,17 +165,8 @@ class SchedulerModel:
             self.running.append(r)
             self.waiting.popleft()
             rec.admitted.append(r.rid)
-        # 3a. prompts are written one chunk per request per step
+        # 3a. every decoding request appends one token (preempting when out of blocks)
         decoders = [r for r in self.running if r.ready]
-        for r in self.running:
-            if r.prefilled < r.prompt_eff:
-                c = min(self.chunk, r.prompt_eff - r.prefilled)
-                rec.prefill.append((r.rid, r.prefilled, c,
-                                    self.alloc.slots(r.rid, r.prefilled, c)))
-                r.prefilled += c
-                if prefix:
-                    self.alloc.register(r.rid, r.tokens[:r.prefilled])
-        # 3b. every decoding request appends one token (preempting when out of blocks)
         for r in decoders:
             while r in self.running:
                 try:
@@ -198,6 +192,16 @@ class SchedulerModel:
                 if prefix:
                     r.tokens.append(self.gen_token(r.rid, pos))
                 break
+        # 3b. prompts still running are written one chunk per request per step; a
+        # request preempted by an append above has no chunk here
+        for r in self.running:
+            if r.prefilled < r.prompt_eff:
+                c = min(self.chunk, r.prompt_eff - r.prefilled)
+                rec.prefill.append((r.rid, r.prefilled, c,
+                                    self.alloc.slots(r.rid, r.prefilled, c)))
+                r.prefilled += c
+                if prefix:
+                    self.alloc.register(r.rid, r.tokens[:r.prefilled])
         if prefix:
             running = {r.rid: r for r in self.running}
             for rid, *_ in rec.decode:

@@ -9,24 +9,27 @@ Batching原理与实践", section 2.3):
 2. arrivals queue up behind the waiting requests, which are admitted first come,
    first served while the whole prompt fits in the free blocks (the first one
    that does not fit blocks the queue);
-3. every running request whose prompt is not yet written gets its next chunk of
-   at most `chunk` prompt tokens, in admission order; a request whose prompt was
-   complete before this step appends one decode token; when no block is free
-   for an append, the running request admitted last is preempted: its blocks
-   are released and it rejoins the head of the queue to recompute its prompt
-   plus the tokens it has generated (hihuo.com page, Preemption（抢占）).
+3. a request whose prompt was complete before this step appends one decode
+   token, in admission order; when no block is free for an append, the running
+   request admitted last is preempted: its blocks are released and it rejoins
+   the head of the queue to recompute its prompt plus the tokens it has
+   generated (hihuo.com page, Preemption（抢占）);
+4. every request still running whose prompt is not yet written gets its next
+   chunk of at most `chunk` prompt tokens, in admission order (after the
+   appends, so that no preempted request keeps a chunk of this step).
 
 With prefix caching (``gen_token`` given), arrivals carry their prompts' token
 IDs; admission reuses the cached opening of each prompt through the allocator's
 ``add_prefix`` (hihuo.com page, 优势 > 3. 支持共享), prefill starts after it, each
-planned chunk's full blocks are registered, and after the decode appends every
-decoding request's newly full blocks are registered, in admission order.
+planned chunk's full blocks are registered, and then every decoding request's
+newly full blocks are registered, in admission order.
 
 With a host pool (``num_host_blocks`` > 0) a preempted request is swapped out
 when the pool can hold it (hihuo.com page, Preemption（抢占）: Swap), else
 recomputed; swapped requests come back first, in swap-out order, before any new
-admission.  The caller runs a step's device work in the order: swap-in copies,
-prompt writes and prefill, swap-out copies, decode writes and decode.
+admission.  A request swapped out in a step has no chunk planned in it.  The
+caller runs a step's device work in the order: swap-in copies, prompt writes
+and prefill, swap-out copies, decode writes and decode.
 
 The plan a step returns says which slots to write and which sequences to decode;
 the caller performs the device work (cache writes, then attention).
@@ -160,13 +163,6 @@ class TraceScheduler:
             self.waiting.popleft()
             plan.admitted.append(r.rid)
         decoders = [r for r in self.running if r.ready]
-        for r in self.running:
-            if r.prefilled < r.prompt_eff:
-                c = min(self.chunk, r.prompt_eff - r.prefilled)
-                plan.prefill.append((r.rid, r.prefilled, c, alloc.slots(r.rid, r.prefilled, c)))
-                r.prefilled += c
-                if prefix:
-                    alloc.register(r.rid, r.tokens[:r.prefilled])
         rids, slots, cows, pos = [], [], [], []
         pending = decoders
         while pending:
@@ -199,6 +195,16 @@ class TraceScheduler:
             self.waiting.appendleft(victim)
             plan.preempted.append(victim.rid)
             pending = [r for r in pending[done:] if r is not victim]
+        # Prompt chunks are planned after the decode appends, so that a request
+        # preempted by an append never holds a planned chunk: its blocks may
+        # already serve the request that needed one.
+        for r in self.running:
+            if r.prefilled < r.prompt_eff:
+                c = min(self.chunk, r.prompt_eff - r.prefilled)
+                plan.prefill.append((r.rid, r.prefilled, c, alloc.slots(r.rid, r.prefilled, c)))
+                r.prefilled += c
+                if prefix:
+                    alloc.register(r.rid, r.tokens[:r.prefilled])
         if prefix:
             # only a token that completes a block can add one to the cache; the
             # other calls would change nothing

@@ -114,6 +114,43 @@ def test_library_scheduler_equals_model_on_trace(num_blocks, steps):
         assert preempted > 0, "the small pool was meant to force preemption"
 
 
+@pytest.mark.parametrize("name,num_blocks,host,steps", [("trace_13b", 3000, 0, 120),
+                                                        ("trace_13b", 3000, 600, 120),
+                                                        ("trace_prefix", 6000, 0, 120)])
+def test_planned_writes_belong_to_requests_still_resident(name, num_blocks, host, steps):
+    """Every slot a step's plan asks the caller to write (prompt chunks and decode
+    tokens) still belongs to its request once the step is planned: a request
+    preempted by a decode append has no chunk in that step, so its freed blocks
+    (which an append may take at once) are never written for it.  No slot is
+    planned twice in one step."""
+    cfg = CONFIGS[name]
+    order = gen.pool_permutation(cfg.seed, num_blocks)
+    gt = cfg.gen_token if cfg.prefix else None
+    lib = TraceScheduler(num_blocks, cfg.block_size, cfg.chunk, order, gen_token=gt,
+                         num_host_blocks=host)
+    same_step = 0
+    for n in range(steps):
+        arr = cfg.arrivals(n) if cfg.prefix else list(zip(*[
+            x.tolist() for x in gen.trace_arrivals(cfg.seed, n, cfg.arrival_mean, cfg.prompt_lo,
+                                                   cfg.prompt_hi, cfg.out_p, cfg.out_lo,
+                                                   cfg.out_hi)]))
+        plan = lib.step(n, arr)
+        resident = set(lib.running_ids())
+        written = []
+        for rid, start, count, slots in plan.prefill:
+            assert rid in resident, (n, rid)
+            assert list(lib.alloc.slots(rid, start, count)) == list(slots), (n, rid)
+            written.extend(int(x) for x in slots)
+        for rid, pos, slot in zip(plan.decode_rids, plan.decode_pos, plan.decode_slots):
+            assert int(rid) in resident, (n, int(rid))
+            assert int(lib.alloc.slots(int(rid), int(pos), 1)[0]) == int(slot), (n, int(rid))
+            written.append(int(slot))
+        assert len(written) == len(set(written)), n
+        gone = set(plan.preempted) | {r for r, _ in plan.swapped_out}
+        same_step += len(gone & set(plan.admitted))
+    assert same_step > 0, "no request was admitted and preempted in one step: the case is not covered"
+
+
 def _plan_cached(plan):
     return [(int(r), int(c)) for r, c in plan.cached]
 
