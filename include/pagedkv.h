@@ -37,7 +37,8 @@ typedef enum pa_status {
     PA_ERR_UNSUPPORTED = 2,  /* valid request outside the compiled shapes / dtypes        */
     PA_ERR_OOM = 3,          /* allocator: not enough free blocks; state unchanged          */
     PA_ERR_STATE = 4,        /* allocator: unknown / duplicate / already-freed sequence     */
-    PA_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed                  */
+    PA_ERR_HIP = 5,          /* a HIP runtime call or kernel launch failed                  */
+    PA_ERR_TOO_LARGE = 6     /* the request needs more than a fixed-size static buffer holds */
 } pa_status;
 
 typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
@@ -252,6 +253,31 @@ pa_status pa_paged_attn_decode_merge(const pa_cache_desc* desc, void* out, const
                                      int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_blocks_per_seq, float scale, int32_t num_units,
                                      void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * pa_paged_attn_decode_noalloc - pa_paged_attn_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  It takes no workspace: partial records and
+ * arrival counts live in one static device buffer of the library,
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES bytes per GPU, held until the process ends.
+ * Arguments, results (bit for bit, for the same num_units) and errors are those of
+ * pa_paged_attn_decode, plus:
+ *   - PA_ERR_TOO_LARGE when pa_decode_workspace_bytes(desc, num_q_heads,
+ *     num_units) exceeds the buffer (nothing is launched then);
+ *   - the first call on a device looks the buffer up (hipGetSymbolAddress) and
+ *     zero-fills it with a kernel on `stream`; no call allocates or frees memory;
+ *   - every call on one GPU shares that GPU's buffer: calls that overlap in time
+ *     on one GPU (different streams, threads or processes' graphs) race and give
+ *     unspecified results.  Calls ordered on one stream are safe; each completed
+ *     call leaves the arrival counts at zero for the next.
+ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+pa_status pa_paged_attn_decode_noalloc(const pa_cache_desc* desc, void* out, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t max_blocks_per_seq, float scale,
+                                       int32_t num_units, uint32_t flags, void* stream);
 
 /*
  * Chunked-prefill attention over the paged cache.

@@ -19,8 +19,11 @@ c_u32 = ctypes.c_uint32
 P_i32, P_i64 = ctypes.POINTER(c_i32), ctypes.POINTER(c_i64)
 
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM",
-                4: "PA_ERR_STATE", 5: "PA_ERR_HIP"}
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_STATE, PA_ERR_HIP = range(6)
+                4: "PA_ERR_STATE", 5: "PA_ERR_HIP", 6: "PA_ERR_TOO_LARGE"}
+(PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_STATE, PA_ERR_HIP,
+ PA_ERR_TOO_LARGE) = range(7)
+# PA_DECODE_NOALLOC_SCRATCH_BYTES: size of the static buffer behind pa_paged_attn_decode_noalloc
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class PagedKVError(RuntimeError):
@@ -52,6 +55,8 @@ SIGNATURES = {
                                      c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_vp]),
     "pa_paged_attn_decode_partial": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                              c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_vp]),
+    "pa_paged_attn_decode_noalloc": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                             c_i32, c_i32, c_f32, c_i32, c_u32, c_vp]),
     "pa_paged_attn_decode_merge": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                            c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_vp]),
     "pa_paged_attn_prefill": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pagedkv.h"
 #include "pagedkv_internal.h"
@@ -78,11 +79,12 @@ const char* pa_status_string(pa_status s) {
         case PA_ERR_OOM: return "out of free blocks";
         case PA_ERR_STATE: return "unknown, duplicate or already-freed sequence";
         case PA_ERR_HIP: return "HIP runtime error";
+        case PA_ERR_TOO_LARGE: return "request needs more than the library's static scratch buffer holds";
     }
     return "unknown status";
 }
 
-int32_t pa_abi_version(void) { return (1 << 16) | 0; }
+int32_t pa_abi_version(void) { return (1 << 16) | 1; }
 
 size_t pa_cache_bytes(const pa_cache_desc* d) {
     if (check_desc(d) != PA_OK) return 0;
@@ -212,14 +214,67 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc* d, int32_t num_q_heads, in
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------------
+// The static scratch buffer of pa_paged_attn_decode_noalloc: one per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per device
+// (with that device current) and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
-// Validation and argument packing shared by the three decode entry points.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ __launch_bounds__(256) void zero_words(uint32_t* __restrict__ p, size_t n) {
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * 256)
+        p[i] = 0u;
+}
+
+// The current device's copy of `scratch`.  The first call on a device looks up its
+// address and zero-fills it with a kernel on `stream` (a fill kernel rather than a
+// memset node, so that a caller may capture the call); the arrival counts at its end
+// then start at zero, and every completed decode leaves them zero again.
+pa_status static_scratch(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return PA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return PA_ERR_HIP;
+        }
+        const size_t words = PA_DECODE_NOALLOC_SCRATCH_BYTES / 4;
+        hipLaunchKernelGGL(zero_words, dim3(1024), dim3(256), 0, stream, static_cast<uint32_t*>(p),
+                           words);
+        if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// Validation and argument packing shared by the decode entry points.  With
+// use_scratch the workspace arguments are ignored and the library's static
+// scratch buffer serves instead (after the request is checked against its size).
 pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                       int32_t max_blocks_per_seq, float scale, int32_t num_units, void* workspace,
-                      size_t workspace_bytes, uint32_t flags, void* stream, int passes) {
+                      size_t workspace_bytes, uint32_t flags, void* stream, int passes,
+                      bool use_scratch = false) {
     pa_status st = check_desc(d);
     if (st != PA_OK) return st;
     if ((flags & ~static_cast<uint32_t>(PA_DECODE_KEEP_CACHED)) != 0) return PA_ERR_INVALID_ARG;
@@ -234,13 +289,20 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     if (max_blocks_per_seq == 0) return PA_ERR_INVALID_ARG;
-    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !workspace)
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens ||
+        (!use_scratch && !workspace))
         return PA_ERR_INVALID_ARG;
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-        !aligned(workspace, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        (!use_scratch && !aligned(workspace, 16)) || !aligned(block_tables, 4) ||
+        !aligned(context_lens, 4))
         return PA_ERR_INVALID_ARG;
     const int32_t units = num_units == 0 ? pa_decode_default_units() : num_units;
-    if (workspace_bytes < workspace_for(d, num_q_heads, units)) return PA_ERR_INVALID_ARG;
+    if (use_scratch) {
+        if (workspace_for(d, num_q_heads, units) > PA_DECODE_NOALLOC_SCRATCH_BYTES)
+            return PA_ERR_TOO_LARGE;
+    } else if (workspace_bytes < workspace_for(d, num_q_heads, units)) {
+        return PA_ERR_INVALID_ARG;
+    }
     const int32_t tpb = d->block_size / pkv::kTile;
     const int32_t rows = use_group ? d->num_kv_heads : num_q_heads;
     // Every tile position of the batch (rows x sequences x table columns) must fit in int32.
@@ -249,6 +311,12 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     // Tile indices into the cache (block * Hkv + head) * tpb + tile are int32 in the kernels.
     if (static_cast<double>(d->num_blocks) * d->num_kv_heads * tpb >= 2147483647.0)
         return PA_ERR_UNSUPPORTED;
+
+    if (use_scratch) {
+        const pa_status ss = static_scratch(static_cast<hipStream_t>(stream), &workspace);
+        if (ss != PA_OK) return ss;
+        workspace_bytes = PA_DECODE_NOALLOC_SCRATCH_BYTES;
+    }
 
     pkv::DecodeArgs a;
     a.q = q;
@@ -315,6 +383,17 @@ pa_status pa_paged_attn_decode_partial(const pa_cache_desc* d, void* out, const 
     return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                        num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
                        workspace_bytes, flags, stream, 1);
+}
+
+pa_status pa_paged_attn_decode_noalloc(const pa_cache_desc* d, void* out, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t max_blocks_per_seq, float scale,
+                                       int32_t num_units, uint32_t flags, void* stream) {
+    return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                       num_q_heads, max_blocks_per_seq, scale, num_units, nullptr, 0, flags,
+                       stream, 3, /*use_scratch=*/true);
 }
 
 pa_status pa_paged_attn_decode_merge(const pa_cache_desc* d, void* out, const void* q,

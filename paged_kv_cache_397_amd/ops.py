@@ -241,6 +241,30 @@ def paged_attn_decode_merge(spec: CacheSpec, out, q, k_cache, v_cache, block_tab
                    context_lens, scale, num_units, workspace, stream, keep_cached)
 
 
+def paged_attn_decode_noalloc(spec: CacheSpec, out, q, k_cache, v_cache, block_tables,
+                              context_lens, scale: float | None = None, num_units: int = 0,
+                              stream=None, keep_cached: bool = False):
+    """paged_attn_decode without a workspace: the library's static per-GPU scratch
+    buffer serves instead (PA_ERR_TOO_LARGE when the request needs more than it
+    holds).  Calls that overlap in time on one GPU race."""
+    S, Hq, D = q.shape
+    if D != spec.head_dim or tuple(out.shape) != (S, Hq, D):
+        raise ValueError("q and out must be [S, Hq, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [S, maxB] and context_lens [S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = N.lib().pa_paged_attn_decode_noalloc(
+        ctypes.byref(spec.desc()), _dev(out, "out", spec.torch_dtype),
+        _dev(q, "q", spec.torch_dtype), _dev(k_cache, "k_cache", spec.torch_dtype),
+        _dev(v_cache, "v_cache", spec.torch_dtype),
+        _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, block_tables.shape[1],
+        float(scale), int(num_units), DECODE_KEEP_CACHED if keep_cached else 0, _stream(stream))
+    N.check(st, "pa_paged_attn_decode_noalloc")
+    return out
+
+
 def paged_attn_prefill(spec: CacheSpec, out, q, k_cache, v_cache, block_tables, query_start,
                        context_lens, scale: float | None = None, max_query_len: int | None = None,
                        stream=None):

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings_and_version():
     lib = N.lib()
-    for s in range(6):
+    for s in range(7):
         assert lib.pa_status_string(s)
     assert lib.pa_status_string(99) == b"unknown status"
     assert lib.pa_abi_version() >> 16 == 1
@@ -80,6 +80,23 @@ def _decode(**kw):
 ])
 def test_decode_host_validation(kw, status):
     assert _decode(**kw) == status
+
+
+def test_noalloc_decode_rejects_requests_beyond_its_static_buffer():
+    """The workspace-free decode checks the request against its static buffer before
+    any device work: G = 16 at D = 128 needs 2 * (16 * 128 + 32) floats per unit, so
+    2048 units need about 34 MB, more than the 16 MiB buffer; validation failures
+    come first, as in the call with a workspace."""
+    lib = N.lib()
+    d = _desc(num_kv_heads=2, head_dim=128)
+    call = lambda Hq, units, out=FAKE: lib.pa_paged_attn_decode_noalloc(
+        ctypes.byref(d), out, FAKE, FAKE, FAKE, FAKE, FAKE, 4, Hq, 3, 0.125, units, 0, None)
+    need = lib.pa_decode_workspace_bytes(ctypes.byref(d), 32, 2048)
+    assert need > N.DECODE_NOALLOC_SCRATCH_BYTES
+    assert call(32, 2048) == N.PA_ERR_TOO_LARGE
+    assert call(32, 2048, out=None) == N.PA_ERR_INVALID_ARG
+    assert call(3, 64) == N.PA_ERR_INVALID_ARG              # Hq % Hkv
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(d), 8, 2048) <= N.DECODE_NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_size_grows_with_units_and_group():
