@@ -192,3 +192,42 @@ def generated_token(seed: int, req: int, position: int, vocab: int) -> int:
     enough to call once per generated token)."""
     x = _splitmix64((int(seed) << 48) ^ (TAG_GEN_TOKEN << 40) ^ (int(req) << 20) ^ int(position))
     return int(x % vocab)
+
+
+# ----------------------------------------------------------------------------- full-size serving-trace values
+
+TAG_TRACE_TABLE = 12   # value tables of the full-size trace parity runs
+_TABLE_ROWS = 4093     # a prime: a request's positions 0 .. 4092 land on distinct rows
+
+
+@functools.lru_cache(maxsize=2)
+def _trace_value_table(seed: int, which: int, width: int, dtype: str) -> np.ndarray:
+    return draw_values(stream(seed, TAG_TRACE_TABLE, which, width), (_TABLE_ROWS, width), dtype)
+
+
+def trace_table_rows(req: int, positions) -> np.ndarray:
+    """Table rows of tokens `positions` of request `req`: (7919 req + 104729 p) mod 4093.
+    Distinct positions of one request (fewer than 4093 apart) get distinct rows."""
+    p = np.asarray(positions, dtype=np.int64).reshape(-1)
+    return (7919 * int(req) + 104729 * p) % _TABLE_ROWS
+
+
+def trace_table_kv(seed: int, req: int, positions, num_kv_heads: int, head_dim: int,
+                   dtype: str):
+    """Keys and values of tokens `positions` of request `req`, two [len, Hkv, D], read
+    from one seeded table of 4093 standard-normal rows (a row holds a token's K and
+    V).  A cheap stand-in for per-token draws at the full trace sizes: a token's
+    values depend only on (seed, req, position), so a recomputed prompt rewrites
+    the same bits; tokens of different requests may share a row."""
+    t = _trace_value_table(seed, 0, 2 * num_kv_heads * head_dim, dtype)
+    x = t[trace_table_rows(req, positions)].reshape(-1, 2, num_kv_heads, head_dim)
+    return np.ascontiguousarray(x[:, 0]), np.ascontiguousarray(x[:, 1])
+
+
+def trace_table_query(seed: int, reqs, positions, num_q_heads: int, head_dim: int,
+                      dtype: str) -> np.ndarray:
+    """Queries [n, Hq, D] of requests `reqs` at the decode steps that write
+    `positions`, from a second seeded table of the same kind."""
+    t = _trace_value_table(seed, 1, num_q_heads * head_dim, dtype)
+    rows = np.array([trace_table_rows(r, [p])[0] for r, p in zip(reqs, positions)], dtype=np.int64)
+    return t[rows].reshape(-1, num_q_heads, head_dim)
