@@ -178,21 +178,18 @@ __global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict_
     tables[static_cast<int64_t>(r) * cols + c] = upd[3 * k + 2];
 }
 
-// One decode step's writes in one launch.  Workgroup (t, h) first copies KV head
-// h's part of the block that token t's copy-on-write pair names (if any), then
-// scatters token t's K and V for head h; every workgroup applies its share of the
-// block-table updates and of the context-length copy.  A head's part of a block is
-// its tile in each of the block's tile slots (tiles are ordered block -> tile ->
-// head), so the copy and the token's write for that head never leave the workgroup.
-// Another token's in-place write into the copy source can land before the copy
-// reads it; it is then carried into the copy at the offset the copying token itself
-// writes next (sequences that share a block hold the same number of tokens in it),
-// so the final bytes equal copy-all, then write-all.  The metadata arrays may live
-// in pinned host memory: each element is read once.
+// One decode step's writes: workgroup (t, h) scatters token t's K and V for head
+// h; every workgroup applies its share of the block-table updates and of the
+// context-length copy.  Copy-on-write copies, when a step has any, run as a
+// launch of their own before this one (launch_append), so every copy reads its
+// source before any token of the step is written and no token write can be
+// overwritten by a copy: the bytes equal copy-all, then write-all, for any slots
+// (several tokens of one sequence in one call included).  The metadata arrays may
+// live in pinned host memory: each element is read once.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void append_tokens_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const int64_t* __restrict__ slots,
-    const int32_t* __restrict__ cow, int num_tokens, T* __restrict__ k_cache,
+    int num_tokens, T* __restrict__ k_cache,
     T* __restrict__ v_cache, int num_kv_heads, int block_size, int num_blocks,
     int32_t* __restrict__ tables, int rows, int cols, const int32_t* __restrict__ upd,
     int num_updates, const int32_t* __restrict__ lens_in, int32_t* __restrict__ lens_out,
@@ -207,8 +204,6 @@ __global__ __launch_bounds__(D) void append_tokens_kernel(
     // from pinned host memory, each dependent read would cost a host-link round trip.
     const bool tok = t < num_tokens;
     const int64_t slot = tok ? slots[t] : -1;
-    const int cow_src = (tok && cow) ? cow[2 * t] : -1;
-    const int cow_dst = (tok && cow) ? cow[2 * t + 1] : -1;
     const int n0 = wg * D + tid;
     const int ur = n0 < num_updates ? upd[3 * n0] : -1;
     const int uc = n0 < num_updates ? upd[3 * n0 + 1] : -1;
@@ -223,28 +218,6 @@ __global__ __launch_bounds__(D) void append_tokens_kernel(
     for (int n = n0 + nwg * D; n < num_lens; n += nwg * D) lens_out[n] = lens_in[n];
     if (!tok) return;
     const int tpb = block_size / kTile;
-    constexpr int tile_u4 = kTile * D * static_cast<int>(sizeof(T)) / 16;  // one tile of one head
-    if (cow) {
-        if (cow_src >= 0 && cow_src < num_blocks && cow_dst >= 0 && cow_dst < num_blocks &&
-            cow_src != cow_dst) {
-            // head h's part of a block: its tile in each of the block's tpb tile slots
-            for (int tt = 0; tt < tpb; ++tt) {
-                const int64_t so = ((static_cast<int64_t>(cow_src) * tpb + tt) * num_kv_heads + h) * tile_u4;
-                const int64_t dof = ((static_cast<int64_t>(cow_dst) * tpb + tt) * num_kv_heads + h) * tile_u4;
-                const u32x4* ks = reinterpret_cast<const u32x4*>(k_cache) + so;
-                const u32x4* vs = reinterpret_cast<const u32x4*>(v_cache) + so;
-                u32x4* kd = reinterpret_cast<u32x4*>(k_cache) + dof;
-                u32x4* vd = reinterpret_cast<u32x4*>(v_cache) + dof;
-                for (int i = tid; i < tile_u4; i += D) {
-                    kd[i] = ks[i];
-                    vd[i] = vs[i];
-                }
-            }
-            // the copy's stores complete before any thread writes the token over them
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-        }
-        __syncthreads();
-    }
     if (slot < 0 || slot >= static_cast<int64_t>(num_blocks) * block_size) return;
     const int64_t b = slot / block_size;
     const int o = static_cast<int>(slot - b * block_size);
@@ -266,11 +239,17 @@ hipError_t launch_append(const void* k, const void* v, const int64_t* slots, con
                          int num_tokens, void* kc, void* vc, int hkv, int bs, int nb,
                          int32_t* tables, int rows, int cols, const int32_t* upd, int n_upd,
                          const int32_t* lens_in, int32_t* lens_out, int n_lens, hipStream_t st) {
+    if (cow && num_tokens > 0) {
+        // every copy-on-write copy completes before any token of the step is written
+        const hipError_t e = launch_copy_blocks(sizeof(T) == 4 ? 0 : 1, D, bs, hkv, nb, kc, vc,
+                                                cow, num_tokens, st);
+        if (e != hipSuccess) return e;
+    }
     const int extra = (n_upd > n_lens ? n_upd : n_lens);
     const dim3 grid = num_tokens > 0 ? dim3(num_tokens, hkv) : dim3((extra + D - 1) / D, 1);
     if (grid.x == 0) return hipSuccess;
     hipLaunchKernelGGL((append_tokens_kernel<T, D>), grid, dim3(D), 0, st,
-                       static_cast<const T*>(k), static_cast<const T*>(v), slots, cow, num_tokens,
+                       static_cast<const T*>(k), static_cast<const T*>(v), slots, num_tokens,
                        static_cast<T*>(kc), static_cast<T*>(vc), hkv, bs, nb, tables, rows, cols,
                        upd, n_upd, lens_in, lens_out, n_lens);
     return hipGetLastError();
