@@ -45,8 +45,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gqa_b256",
                     choices=["gqa_b256", "llama2_7b_b64", "tiny_f32", "shared_prefix_b16", "shared_prefix_b32",
-                             "trace_13b", "trace_prefix", "prefill_13b", "prefill_gqa", "swap_13b", "blocksize_sweep"])
+                             "trace_13b", "trace_prefix", "prefill_13b", "prefill_gqa", "swap_13b", "blocksize_sweep",
+                             "hbm_ceiling"])
     ap.add_argument("--units", type=int, default=0, help="decode work units (0 = library default)")
+    ap.add_argument("--step-launch", choices=["one", "two"], default="two",
+                    help="a decode step as one launch (pa_decode_step: cache writes folded into "
+                         "the decode kernel) or as two (pa_append_tokens, then pa_paged_attn_decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -243,7 +247,9 @@ def run_trace(args):
                                     for s0, c in zip(st.tolist(), cl.tolist())))
         if S:
             d["dslots"] = torch.from_numpy(plan.decode_slots).cuda()
-            d["cows"] = torch.from_numpy(np.ascontiguousarray(plan.decode_cows)).cuda()
+            # a step whose appends copy no block passes no pairs (one write launch)
+            d["cows"] = (torch.from_numpy(np.ascontiguousarray(plan.decode_cows)).cuda()
+                         if (plan.decode_cows[:, 0] >= 0).any() else None)
             d["tables"] = torch.from_numpy(tables).cuda()
             d["ctx"] = torch.from_numpy(ctx).cuda()
             d["k"] = torch.randn(S, Hkv, D, generator=g, device="cuda", dtype=spec.torch_dtype)
@@ -765,6 +771,77 @@ def run_swap(args):
     print(json.dumps(result), flush=True)
 
 
+def run_ceiling(args):
+    """What the part delivers for the decode kernel's read pattern, without any
+    attention work: the probe library's eight-wave workgroups read, per step, one
+    32 KiB chunk of a K buffer and one of a V buffer (each wave its 4 KiB slice,
+    one 16-byte load per lane per KiB), over 1.27 GB (the batch-256 GQA step's
+    K/V).  Streaming = each workgroup walks its own contiguous run of chunks;
+    gather = chunks in a seeded random order.  Non-temporal or ordinary loads, one
+    tile in flight per wave (as decode) or two."""
+    import ctypes
+
+    import torch
+
+    from paged_kv_cache_397_amd import build as B
+
+    if not os.path.exists(B.PROBE_LIB):
+        raise ImportError(f"{B.PROBE_LIB} is missing: build the package first")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    fn = lib.pa_probe_gather_read
+    fn.restype = ctypes.c_int32
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_void_p]
+    chunk = 32 * 1024
+    results = []
+    stream = torch.cuda.current_stream()
+    for groups, per in ((256, 76), (512, 38), (128, 152)):
+        n = groups * per
+        k = torch.empty(n * chunk // 4, dtype=torch.int32, device="cuda")
+        v = torch.empty_like(k)
+        k.fill_(1)
+        v.fill_(2)
+        sink = torch.empty(groups * 8, dtype=torch.int32, device="cuda")
+        rng = np.random.default_rng(12345)
+        orders = {"stream": np.arange(n, dtype=np.int32),
+                  "gather": rng.permutation(n).astype(np.int32)}
+        nbytes = 2.0 * n * chunk
+        for mode, order in orders.items():
+            od = torch.from_numpy(order).cuda()
+            for nt in (1, 0):
+                for inflight in (1, 2):
+                    call = lambda: fn(k.data_ptr(), v.data_ptr(), n, od.data_ptr(), groups, per,
+                                      sink.data_ptr(), nt, inflight, stream.cuda_stream)
+                    times = []
+                    for rep in range(13):
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        rc = call()
+                        e1.record(stream)
+                        if rc != 0:
+                            raise RuntimeError(f"probe launch failed ({rc})")
+                        torch.cuda.synchronize()
+                        if rep >= 3:
+                            times.append(e0.elapsed_time(e1) * 1e-3)
+                    t = float(np.median(times))
+                    results.append({"waves": groups * 8, "mode": mode,
+                                    "loads": "non-temporal" if nt else "ordinary",
+                                    "tiles_in_flight": inflight, "us": round(t * 1e6, 2),
+                                    "gbps": round(nbytes / t / 1e9, 1),
+                                    "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)})
+                    log(f"{results[-1]}")
+        del k, v
+        torch.cuda.empty_cache()
+    best = max(r["gbps"] for r in results if r["mode"] == "gather")
+    print(json.dumps({"metric": "read ceiling for the decode access pattern (probe, no attention)",
+                      "value": best, "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+                      "config": {"workload": "hbm_ceiling: 2 x 32 KiB chunks per workgroup step, "
+                                             "1.27 GB per pass"},
+                      "bytes_per_pass": int(2 * 256 * 76 * chunk), "runs": results}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -786,6 +863,9 @@ def main():
         return
     if args.config == "blocksize_sweep":
         run_blocksize(args)
+        return
+    if args.config == "hbm_ceiling":
+        run_ceiling(args)
         return
     if args.config == "tiny_f32":
         run_tiny(args)
@@ -854,10 +934,12 @@ def main():
         vs.append(to_device(vn, spec))
     out = torch.empty(S, Hq, D, dtype=spec.torch_dtype, device="cuda")
     units = args.units if args.units > 0 else ops.default_units()
-    ws = ops.decode_workspace(spec, Hq, units)
+    one_launch = args.step_launch == "one"
+    ws = (ops.decode_step_workspace(spec, Hq, S, units) if one_launch
+          else ops.decode_workspace(spec, Hq, units))
     torch.cuda.synchronize()
     log(f"inputs resident in HBM ({time.time() - t0:.1f} s): {S} seqs, sum ctx {int(ctx0.sum())}, "
-        f"{units} units")
+        f"{units} units, step as {'one launch' if one_launch else 'two launches'}")
 
     # ---------------------------------------------------------------- per-step staging
     # A ring of pinned host buffers holds each step's metadata; the cache-write
@@ -885,17 +967,32 @@ def main():
 
     # Every launch of every step is bound once (arguments converted up front); the
     # per-step metadata has a fixed shape (a copy-on-write row and a table-update row
-    # per sequence, -1 when there is none), so a step's launches never change form.
+    # per sequence, -1 when there is none).  A step whose appends copy no block
+    # passes no copy-on-write pairs, so its writes are one launch; a step with
+    # copies runs them as a launch of their own first.
     # Sequences forked from one parent share its blocks: those are read with ordinary
     # loads so that the shared prefix stays cached; private contexts are streamed.
+    # With one launch per step (pa_decode_step) the decode kernel itself writes each
+    # sequence's new token (and a copy-on-write copy) from the pinned metadata, sets
+    # the table entries and lengths, and attends.
     shared = cfg.ctx_kind == "shared_prefix"
     calls = []
     for n in range(total_steps):
         hs, hc, hu, hp = views(pin[n % R])
+        if one_launch:
+            step_args = (spec, out, qs[n], ks[n], vs[n], hs, hc, cache.k, cache.v, tables, ctx_dev)
+            calls.append((
+                ops.bind_decode_step(*step_args, scale=cfg.scale, num_units=units, workspace=ws,
+                                     keep_cached=shared),
+                ops.bind_decode_step(*step_args, cow_pairs=hp, scale=cfg.scale, num_units=units,
+                                     workspace=ws, keep_cached=shared),
+                None))
+            continue
+        write_args = dict(block_tables=tables, table_updates=hu, lens_in=hc, lens_out=ctx_dev)
         calls.append((
+            ops.bind_append_tokens(spec, ks[n], vs[n], hs, cache.k, cache.v, **write_args),
             ops.bind_append_tokens(spec, ks[n], vs[n], hs, cache.k, cache.v, cow_pairs=hp,
-                                   block_tables=tables, table_updates=hu, lens_in=hc,
-                                   lens_out=ctx_dev),
+                                   **write_args),
             ops.bind_decode(spec, out, qs[n], cache.k, cache.v, tables, ctx_dev, cfg.scale, units,
                             ws, keep_cached=shared)))
 
@@ -931,14 +1028,18 @@ def main():
         pu[:, 2] = nb
         pp[:] = cows  # one (src, dst) row per token, (-1, -1) = no copy
         h1 = time.perf_counter()
-        append, decode = calls[n]
+        plain, with_cow, decode = calls[n]
+        append = with_cow if (cows[:, 0] >= 0).any() else plain
+        if decode is None:  # one launch: the step call does the writes and the decode
+            append, decode = (lambda: None), append
         timing = mode == "profile" or (mode == "timed" and (n - warm) % 5 == 0)
         if timing:
             e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         if mode == "profile":
             e0.record(stream)
         # a3 + a4: copy-on-write block copies, the changed table entries, the cache
-        # write of the step's new tokens and the context lengths, in one launch
+        # write of the step's new tokens and the context lengths (a launch of their
+        # own with two launches per step)
         append()
         if timing:
             e1.record(stream)
@@ -991,7 +1092,14 @@ def main():
     # evict and write back) and right after reading it (clean lines only).
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     flush.fill_(1.0)
-    _, last_decode = calls[total_steps - 1]
+    if one_launch:
+        # the cold runs repeat the last step's attention with the plain decode call
+        # (same kernel without the writes): the step itself would append again
+        ws_cold = ops.decode_workspace(spec, Hq, units)
+        last_decode = ops.bind_decode(spec, out, qs[total_steps - 1], cache.k, cache.v, tables,
+                                      ctx_dev, cfg.scale, units, ws_cold, keep_cached=shared)
+    else:
+        last_decode = calls[total_steps - 1][2]
     cold = {"write": [], "read": []}
     for kind in ("write", "read"):
         for _ in range(5):
@@ -1051,7 +1159,8 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.title}", "seqs": S, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": D, "block_size": B, "pool_blocks": cfg.num_blocks,
                    "sum_ctx_first_step": int(tok[0]), "units": units, "seed": cfg.seed,
-                   "kv_loads": "cached (shared blocks)" if shared else "streamed (non-temporal)"},
+                   "kv_loads": "cached (shared blocks)" if shared else "streamed (non-temporal)",
+                   "step_launches": 1 if one_launch else 2},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "shared_prefix_unique": unique,
         "us_per_step": round(wall / steps * 1e6, 2),
@@ -1086,7 +1195,9 @@ def main():
                      "staging = writing the step's metadata into its pinned ring slot; ring wait = "
                      "waiting for the GPU to free that slot (the host runs ahead of the GPU)",
         "roofline": {
-            "kernel": "decode_pass1 (gather + attention, merge of split sequences folded in)",
+            "kernel": ("decode_pass1, decode-step form (the step's cache writes, gather + attention, "
+                       "merge of split sequences, one cooperative launch)" if one_launch else
+                       "decode_pass1 (gather + attention, merge of split sequences folded in)"),
             "bound": "hbm",
             "achieved": round(dec_gbps, 2),
             "peak": HBM_PEAK_GBPS,

@@ -130,11 +130,12 @@ pa_status pa_update_block_tables(int32_t* block_tables, int32_t num_rows,
                                  int32_t num_updates, void* stream);
 
 /*
- * pa_append_tokens - every write of one decode step in a single launch: the
- * copy-on-write block copies, the block-table updates, the new tokens' scatter
- * (the writes that follow each forward step, [P2] 调度流程 step 4; the sharing
- * that copy-on-write preserves, [P2] 优势 > 3. 支持共享) and the upload of the
- * context lengths the next decode call reads.
+ * pa_append_tokens - every write of one decode step: the copy-on-write block
+ * copies, the block-table updates, the new tokens' scatter (the writes that
+ * follow each forward step, [P2] 调度流程 step 4; the sharing that copy-on-write
+ * preserves, [P2] 优势 > 3. 支持共享) and the upload of the context lengths the
+ * next decode call reads.  One launch when cow_pairs is NULL; with cow_pairs the
+ * copies run as a first launch, so pass NULL for a step that copies nothing.
  *   k, v, slot_mapping, num_tokens   as for pa_reshape_and_cache
  *   cow_pairs      [num_tokens][2] int32 (src, dst) or NULL: before token t is
  *                  written, block src is copied onto block dst (whole block, K and
@@ -146,10 +147,9 @@ pa_status pa_update_block_tables(int32_t* block_tables, int32_t num_rows,
  *                  (lens_out device; NULL/0 = nothing)
  * slot_mapping, cow_pairs, table_updates and lens_in may be device memory or
  * pinned host memory (each element is read once), so a step's host-built
- * metadata needs no separate copy.  The result equals pa_copy_blocks (all pairs),
- * pa_update_block_tables, then pa_reshape_and_cache, provided that sequences
- * which share a block hold the same number of tokens in it (always the case for
- * blocks shared through the allocator's fork).
+ * metadata needs no separate copy.  The result equals pa_copy_blocks (all valid
+ * pairs), pa_update_block_tables, then pa_reshape_and_cache, under those calls'
+ * preconditions; any number of a sequence's tokens may be written in one call.
  */
 pa_status pa_append_tokens(const pa_cache_desc* desc, const void* k, const void* v,
                            const int64_t* slot_mapping, const int32_t* cow_pairs,
@@ -253,6 +253,48 @@ pa_status pa_paged_attn_decode_merge(const pa_cache_desc* desc, void* out, const
                                      int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_blocks_per_seq, float scale, int32_t num_units,
                                      void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * pa_decode_step - one decode step of a layer in one launch: the writes of
+ * pa_append_tokens and the attention of pa_paged_attn_decode together.  After
+ * each forward step every running sequence appends its new token and the next
+ * step attends over it ([P2] 调度流程; [P1] section 2: decode runs one step per
+ * token and is the bottleneck), so both happen every step; here the token is
+ * taken into attention straight from k_new / v_new and written to the cache by
+ * the same waves that read its tile, with no separate write launch.
+ *   k_new, v_new   device, [num_seqs, Hkv, D]: sequence i's new token (position
+ *                  lens_in[i] - 1), dtype of the cache, 16-B aligned
+ *   slot_mapping   [num_seqs] int64, device or pinned host: the slot of that
+ *                  position (its offset must be (lens_in[i] - 1) % B); -1 = the
+ *                  sequence writes no token this step (attended as cached)
+ *   cow_pairs      [num_seqs][2] int32 (src, dst) or NULL, device or pinned host:
+ *                  sequence i's last block is copied from src onto dst (= the
+ *                  block of its slot) before its token is written; (-1, -1) = none
+ *   lens_in        [num_seqs] int32, device or pinned host: context lengths
+ *                  including the new token; copied into context_lens
+ *   block_tables, context_lens   device, as in pa_paged_attn_decode; updated in
+ *                  place: block_tables[i][(lens_in[i] - 1) / B] = slot / B and
+ *                  context_lens = lens_in, as the next call expects them
+ *   workspace      pa_decode_step_workspace_bytes(desc, Hq, num_units, num_seqs)
+ *                  bytes, zero-filled once (the same rules as for
+ *                  pa_paged_attn_decode's workspace; a workspace sized for the
+ *                  step also serves pa_paged_attn_decode with the same bytes)
+ * Results: cache bytes, tables and lengths equal those of pa_append_tokens(k_new,
+ * v_new, slot_mapping, cow_pairs, the table entries above, lens_in -> context_lens)
+ * and out equals, bit for bit, the pa_paged_attn_decode call that follows it
+ * (same num_units and flags).  Inside the launch, workgroup 0 writes the lengths
+ * and table entries and every other workgroup waits (bounded) until it has; other
+ * arguments and errors as in pa_paged_attn_decode.
+ */
+size_t pa_decode_step_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
+                                      int32_t num_units, int32_t num_seqs);
+pa_status pa_decode_step(const pa_cache_desc* desc, void* out, const void* q, const void* k_new,
+                         const void* v_new, const int64_t* slot_mapping, const int32_t* cow_pairs,
+                         const int32_t* lens_in, void* k_cache, void* v_cache,
+                         int32_t* block_tables, int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t max_blocks_per_seq, float scale,
+                         int32_t num_units, void* workspace, size_t workspace_bytes,
+                         uint32_t flags, void* stream);
 
 /*
  * pa_paged_attn_decode_noalloc - pa_paged_attn_decode for callers that cannot

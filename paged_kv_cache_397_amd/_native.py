@@ -55,6 +55,9 @@ SIGNATURES = {
                                      c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_vp]),
     "pa_paged_attn_decode_partial": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                              c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_vp]),
+    "pa_decode_step_workspace_bytes": (c_sz, [P_desc, c_i32, c_i32, c_i32]),
+    "pa_decode_step": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                               c_vp, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_vp]),
     "pa_paged_attn_decode_noalloc": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                              c_i32, c_i32, c_f32, c_i32, c_u32, c_vp]),
     "pa_paged_attn_decode_merge": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,

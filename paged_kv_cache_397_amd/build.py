@@ -21,10 +21,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedkv.so")
+# A read-bandwidth probe with the decode kernel's access pattern, for measuring the
+# part's ceiling; a library of its own, never loaded by the paged-attention path.
+PROBE_LIB = os.path.join(PKG, "libpagedkv_probe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.cpp", "allocator.cpp", "kernels_cache.hip", "kernels_decode.hip",
            "kernels_prefill.hip"]
+PROBE_SOURCES = ["bandwidth_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -49,24 +53,27 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libpagedkv.so; return its path."""
+    """Compile every source, link libpagedkv.so and libpagedkv_probe.so; return the
+    path of libpagedkv.so."""
     hipcc = _hipcc()
     os.makedirs(OBJ_DIR, exist_ok=True)
     common = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-Wall", "-Wno-unused-function"]
-    objs = []
+    objs = {}
     cmds = []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-        objs.append(obj)
+        objs[src] = obj
         lang = ["-x", "hip"] if src.endswith(".hip") or src == "api.cpp" else ["-x", "c++"]
         cmds.append([hipcc, *common, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[objs[s] for s in srcs],
+              "-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -30,7 +30,10 @@ size_t elem_bytes(const pa_cache_desc* d) { return d->dtype == PA_DTYPE_F32 ? 4 
 
 pa_status from_hip(hipError_t e) {
     if (e == hipSuccess) return PA_OK;
-    if (e == hipErrorInvalidValue) return PA_ERR_UNSUPPORTED;
+    if (e == hipErrorInvalidValue) {
+        (void)hipGetLastError();
+        return PA_ERR_UNSUPPORTED;
+    }
     return PA_ERR_HIP;
 }
 
@@ -42,20 +45,28 @@ bool group_kernel_for(const pa_cache_desc* d, int32_t group) {
 // start; W split counts, from the end (count i is the i-th int32 before the end), so
 // that calls with different unit counts on one workspace never write each other's
 // counts.
+// A decode step (pa_decode_step) also keeps, after the unit records, a 16-byte
+// sync word block and 16 bytes of metadata per sequence.
 struct WorkspaceLayout {
     size_t piece_floats;  // floats of one partial record
     size_t rec_offset;    // bytes to the unit records
+    size_t step_offset;   // bytes to the decode step's sync words, then its per-sequence metadata
     size_t bytes;         // total
 };
 
-WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t num_q_heads, int32_t units) {
+WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t num_q_heads, int32_t units,
+                                 int32_t step_seqs = -1) {
     const int32_t group = num_q_heads / d->num_kv_heads;
     const int32_t gh = group_kernel_for(d, group) ? group : 1;
     WorkspaceLayout w;
     w.piece_floats = static_cast<size_t>(gh) * d->head_dim + ((2 * gh + 3) & ~3);
     const size_t pieces = static_cast<size_t>(units) * 2 * w.piece_floats * sizeof(float);
     w.rec_offset = (pieces + 255) & ~size_t(255);
-    w.bytes = w.rec_offset + static_cast<size_t>(units) * (pkv::kRecInts + 1) * sizeof(int32_t);
+    const size_t recs = static_cast<size_t>(units) * pkv::kRecInts * sizeof(int32_t);
+    w.step_offset = (w.rec_offset + recs + 15) & ~size_t(15);
+    const size_t step = step_seqs < 0 ? 0 : 16 + static_cast<size_t>(step_seqs) * 16;
+    w.bytes = (step_seqs < 0 ? w.rec_offset + recs : w.step_offset + step) +
+              static_cast<size_t>(units) * sizeof(int32_t);
     return w;
 }
 
@@ -266,15 +277,26 @@ pa_status static_scratch(hipStream_t stream, void** out) {
 
 namespace {
 
+// The step's writes that pa_decode_step folds into the decode launch.
+struct StepIO {
+    const void* k_new;
+    const void* v_new;
+    const int64_t* slots;
+    const int32_t* cow;
+    const int32_t* lens_in;
+};
+
 // Validation and argument packing shared by the decode entry points.  With
 // use_scratch the workspace arguments are ignored and the library's static
 // scratch buffer serves instead (after the request is checked against its size).
+// With step, the call is a decode step (pa_decode_step): one launch that also
+// performs the step's cache writes.
 pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                       int32_t max_blocks_per_seq, float scale, int32_t num_units, void* workspace,
                       size_t workspace_bytes, uint32_t flags, void* stream, int passes,
-                      bool use_scratch = false) {
+                      bool use_scratch = false, const StepIO* step = nullptr) {
     pa_status st = check_desc(d);
     if (st != PA_OK) return st;
     if ((flags & ~static_cast<uint32_t>(PA_DECODE_KEEP_CACHED)) != 0) return PA_ERR_INVALID_ARG;
@@ -296,11 +318,17 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
         (!use_scratch && !aligned(workspace, 16)) || !aligned(block_tables, 4) ||
         !aligned(context_lens, 4))
         return PA_ERR_INVALID_ARG;
+    if (step) {
+        if (!step->k_new || !step->v_new || !step->slots || !step->lens_in ||
+            !aligned(step->k_new, 16) || !aligned(step->v_new, 16) || !aligned(step->slots, 8) ||
+            !aligned(step->lens_in, 4) || (step->cow && !aligned(step->cow, 4)))
+            return PA_ERR_INVALID_ARG;
+    }
     const int32_t units = num_units == 0 ? pa_decode_default_units() : num_units;
+    const size_t need = workspace_layout(d, num_q_heads, units, step ? num_seqs : -1).bytes;
     if (use_scratch) {
-        if (workspace_for(d, num_q_heads, units) > PA_DECODE_NOALLOC_SCRATCH_BYTES)
-            return PA_ERR_TOO_LARGE;
-    } else if (workspace_bytes < workspace_for(d, num_q_heads, units)) {
+        if (need > PA_DECODE_NOALLOC_SCRATCH_BYTES) return PA_ERR_TOO_LARGE;
+    } else if (workspace_bytes < need) {
         return PA_ERR_INVALID_ARG;
     }
     const int32_t tpb = d->block_size / pkv::kTile;
@@ -326,12 +354,22 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     {
-        const WorkspaceLayout w = workspace_layout(d, num_q_heads, units);
+        const WorkspaceLayout w = workspace_layout(d, num_q_heads, units, step ? num_seqs : -1);
         char* base = static_cast<char*>(workspace);
         a.pieces = reinterpret_cast<float*>(base);
         a.unit_rec = reinterpret_cast<int32_t*>(base + w.rec_offset);
         a.split_count_end = reinterpret_cast<int32_t*>(base + (workspace_bytes & ~size_t(3)));
         a.heads_per_row = use_group ? group : 1;
+        a.lens_in = step ? step->lens_in : nullptr;
+        a.new_slots = step ? step->slots : nullptr;
+        a.cow_in = step ? step->cow : nullptr;
+        a.k_new = step ? step->k_new : nullptr;
+        a.v_new = step ? step->v_new : nullptr;
+        a.lens_dev = step ? const_cast<int32_t*>(context_lens) : nullptr;
+        a.tables_dev = step ? const_cast<int32_t*>(block_tables) : nullptr;
+        a.sync = step ? reinterpret_cast<int32_t*>(base + w.step_offset) : nullptr;
+        a.seq_info = step ? reinterpret_cast<int32_t*>(base + w.step_offset + 16) : nullptr;
+        a.block_size = d->block_size;
     }
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
@@ -341,18 +379,21 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     a.max_blocks = max_blocks_per_seq;
     a.tiles_per_block = tpb;
     a.num_blocks = d->num_blocks;
-    a.num_units = units;
     // Aligned split: with at least one unit per row, every row is cut into the same
     // ranges, and the rows of a range (up to 8, a power of two dividing the row
     // count) share a workgroup.
-    a.fused = passes == 3 ? 1 : 0;
+    a.fused = (passes == 3 || step) ? 1 : 0;
     a.keep_cached = (flags & PA_DECODE_KEEP_CACHED) ? 1 : 0;
 
+    a.num_units = units;
     a.aligned = units >= rows ? 1 : 0;
     a.waves_per_group = 1;
     if (a.aligned)
         while (a.waves_per_group < 8 && rows % (2 * a.waves_per_group) == 0) a.waves_per_group *= 2;
     a.scale_log2e = scale * 1.4426950408889634f;
+    if (step)
+        return from_hip(pkv::launch_decode_step(d->dtype, d->head_dim, use_group, a,
+                                                static_cast<hipStream_t>(stream)));
     return from_hip(pkv::launch_decode(d->dtype, d->head_dim, use_group, a, passes,
                                        static_cast<hipStream_t>(stream)));
 }
@@ -383,6 +424,28 @@ pa_status pa_paged_attn_decode_partial(const pa_cache_desc* d, void* out, const 
     return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                        num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
                        workspace_bytes, flags, stream, 1);
+}
+
+size_t pa_decode_step_workspace_bytes(const pa_cache_desc* d, int32_t num_q_heads,
+                                      int32_t num_units, int32_t num_seqs) {
+    if (check_desc(d) != PA_OK || num_q_heads <= 0 || num_q_heads % d->num_kv_heads != 0 ||
+        num_units < 0 || num_units > kMaxUnits || num_seqs < 0)
+        return 0;
+    const int32_t units = num_units == 0 ? pa_decode_default_units() : num_units;
+    return workspace_layout(d, num_q_heads, units, num_seqs).bytes;
+}
+
+pa_status pa_decode_step(const pa_cache_desc* d, void* out, const void* q, const void* k_new,
+                         const void* v_new, const int64_t* slot_mapping, const int32_t* cow_pairs,
+                         const int32_t* lens_in, void* k_cache, void* v_cache,
+                         int32_t* block_tables, int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t max_blocks_per_seq, float scale,
+                         int32_t num_units, void* workspace, size_t workspace_bytes,
+                         uint32_t flags, void* stream) {
+    const StepIO io{k_new, v_new, slot_mapping, cow_pairs, lens_in};
+    return decode_call(d, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                       num_q_heads, max_blocks_per_seq, scale, num_units, workspace,
+                       workspace_bytes, flags, stream, 3, false, &io);
 }
 
 pa_status pa_paged_attn_decode_noalloc(const pa_cache_desc* d, void* out, const void* q,

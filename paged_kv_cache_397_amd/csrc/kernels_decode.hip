@@ -67,6 +67,10 @@ namespace {
 #if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
 #error "the decode kernels' in-launch merge relies on gfx950 memory behaviour; build for gfx950 only"
 #endif
+// Word 3 of a raw buffer resource on gfx9-family targets: 32-bit data format, no
+// swizzle (the hardware's documented value for untyped buffer loads).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 __device__ __forceinline__ void store_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -529,6 +533,74 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int row, int s
 }
 
 // ---------------------------------------------------------------------------------
+// A decode step's new token inside a tile, for the lanes that hold its place.  Both
+// paths read a tile in one register layout (it follows from the cache layout): lane
+// l = 16 j + i holds, for K load s, token i at dims (4 s + j) X .. (4 s + j) X + X - 1,
+// and for V load m, tokens 4 j .. 4 j + 3 at dims 16 E m + 16 e + i (e < E), each
+// 16-byte group holding for each e the four tokens' values (element e * 4 + token % 4).
+// So for the token at position p of the tile, the lanes with i == p load its K groups
+// from the new row instead of the cache (the tile's own bytes there are not needed),
+// and the lanes with j == p / 4 load one value per (m, e) of its V row, merged into
+// the groups once the tile has arrived.
+template <typename T, int NL>
+struct TokenV {
+    static constexpr int X = 16 / static_cast<int>(sizeof(T));
+    static constexpr int E = X / 4;
+    uint32_t v[NL][E];
+};
+
+// Every lane issues the same loads on every tile (lanes and tiles without the token
+// read a harmless element instead): the number of loads in flight then never
+// depends on the tile, so the compiler's waits for a tile never wait for the next
+// tile's loads as well.
+template <typename T, int NL>
+__device__ __forceinline__ void load_token_v(TokenV<T, NL>& tv, const T* vn, const T* dummy, int p,
+                                             int lane) {
+    constexpr int E = TokenV<T, NL>::E;
+    const int j = lane >> 4, i = lane & 15;
+    const bool mine = p >= 0 && j == (p >> 2);
+    const T* base = mine ? vn + i : dummy;
+    const int stride = mine ? 16 : 0;
+#pragma unroll
+    for (int m = 0; m < NL; ++m)
+#pragma unroll
+        for (int e = 0; e < E; ++e) tv.v[m][e] = static_cast<uint32_t>(base[stride * (E * m + e)]);
+}
+
+template <typename T, int NL>
+__device__ __forceinline__ void patch_token_v(u32x4* vb, const TokenV<T, NL>& tv, int p, int lane) {
+    const int j = lane >> 4;
+    if (j != (p >> 2)) return;
+    const int r = p & 3;
+#pragma unroll
+    for (int m = 0; m < NL; ++m) {
+        u32x4 g = vb[m];
+        if constexpr (sizeof(T) == 2) {
+            // word 2 e + (r >> 1) holds tokens 4 j + 2 (r >> 1) .. + 1 of the e-th dim
+            const bool odd = (r >> 1) != 0, high = (r & 1) != 0;
+            uint32_t w0 = odd ? g[1] : g[0];
+            uint32_t w2 = odd ? g[3] : g[2];
+            w0 = high ? ((w0 & 0xffffu) | (tv.v[m][0] << 16)) : ((w0 & 0xffff0000u) | tv.v[m][0]);
+            w2 = high ? ((w2 & 0xffffu) | (tv.v[m][1] << 16)) : ((w2 & 0xffff0000u) | tv.v[m][1]);
+            if (odd) {
+                g[1] = w0;
+                g[3] = w2;
+            } else {
+                g[0] = w0;
+                g[2] = w2;
+            }
+        } else {
+            // one token per word
+            g[0] = r == 0 ? tv.v[m][0] : g[0];
+            g[1] = r == 1 ? tv.v[m][0] : g[1];
+            g[2] = r == 2 ? tv.v[m][0] : g[2];
+            g[3] = r == 3 ? tv.v[m][0] : g[3];
+        }
+        vb[m] = g;
+    }
+}
+
+// ---------------------------------------------------------------------------------
 // Walking a unit's tiles.  The line of tiles is addressed by a cursor (row,
 // sequence, tile inside the sequence).  A chunk describes up to 64 consecutive
 // tiles of the walk, one per lane, with everything the loop needs to fetch and
@@ -548,14 +620,17 @@ struct Chunk {
     int row;     // lane k: work row
     int ctx;     // lane k: context length of its sequence
     int toff;    // lane k: tile index in the cache, (block * tpb + tile % tpb) * Hkv + kv head
+    int wtoff;   // lane k (decode step): tile index the tile is written to, -1 = none
+    int ptok;    // lane k (decode step): position of the new token in the tile, -1 = none
     Cursor next; // where the walk continues after the chunk (uniform)
 };
 
 // Uniform copy of one lane of a chunk.
 struct TileRef {
-    int seq, tile, row, ctx, toff;
+    int seq, tile, row, ctx, toff, wtoff, ptok;
 };
 
+template <bool Step>
 __device__ __forceinline__ TileRef tile_ref(const Chunk& c, int k) {
     TileRef r;
     r.seq = __builtin_amdgcn_readlane(c.seq, k);
@@ -563,13 +638,20 @@ __device__ __forceinline__ TileRef tile_ref(const Chunk& c, int k) {
     r.row = __builtin_amdgcn_readlane(c.row, k);
     r.ctx = __builtin_amdgcn_readlane(c.ctx, k);
     r.toff = __builtin_amdgcn_readlane(c.toff, k);
+    if constexpr (Step) {
+        r.wtoff = __builtin_amdgcn_readlane(c.wtoff, k);
+        r.ptok = __builtin_amdgcn_readlane(c.ptok, k);
+    } else {
+        r.wtoff = -1;
+        r.ptok = -1;
+    }
     return r;
 }
 
 // The chunk of at most min(64, remaining) tiles starting at cursor c.  Rows wrap
 // after sequence S - 1; sequences with no tiles are passed over.  Block IDs
 // outside [0, N) are replaced by 0 so a bad table never addresses outside the pool.
-template <class Path>
+template <class Path, bool Step>
 __device__ __forceinline__ Chunk build_chunk(const DecodeArgs& a, Cursor c, int remaining,
                                              int lane) {
     const int S = a.num_seqs;
@@ -599,15 +681,40 @@ __device__ __forceinline__ Chunk build_chunk(const DecodeArgs& a, Cursor c, int 
     ch.row = rr;
     ch.tile = tin;
     ch.ctx = __shfl(ctx_k, j);
-    int toff = 0;
+    int toff = 0, wtoff = -1, ptok = -1;
     if (lane < ch.n) {
         const int tpb = a.tiles_per_block;
         const int e = tin / tpb;
         int blk = a.block_tables[static_cast<size_t>(ssk) * a.max_blocks + e];
+        int wblk = -1;
+        if constexpr (Step) {
+            // A tile of the last block of a sequence with a new token: that block (and,
+            // under copy-on-write, the source it is read from) comes from the step's
+            // metadata, not the table.  In place, only the new token's tile is written
+            // back; under copy-on-write every tile of the block goes to the copy.
+            const int c = ch.ctx;
+            if (c > 0 && e == (c - 1) / (tpb * kTile)) {
+                const u32x4 info = *reinterpret_cast<const u32x4*>(a.seq_info + 4 * ssk);
+                const int flags = static_cast<int>(info[2]);
+                if (flags & 1) {
+                    const bool tok_tile = tin == (c - 1) / kTile;
+                    blk = static_cast<int>(info[0]);
+                    if ((flags & 2) || tok_tile) wblk = static_cast<int>(info[1]);
+                    if (tok_tile) ptok = (c - 1) & (kTile - 1);
+                }
+            }
+        }
         blk = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
-        toff = (blk * tpb + (tin - e * tpb)) * a.num_kv_heads + Path::kv_head(a, rr);
+        const int kvh = Path::kv_head(a, rr);
+        toff = (blk * tpb + (tin - e * tpb)) * a.num_kv_heads + kvh;
+        if (static_cast<unsigned>(wblk) < static_cast<unsigned>(a.num_blocks))
+            wtoff = (wblk * tpb + (tin - e * tpb)) * a.num_kv_heads + kvh;
+        else
+            ptok = -1;
     }
     ch.toff = toff;
+    ch.wtoff = wtoff;
+    ch.ptok = ptok;
     // the walk after the chunk
     if (ch.n < avail) {
         const unsigned long long past = __ballot(incl > ch.n);
@@ -631,10 +738,107 @@ __device__ __forceinline__ Chunk build_chunk(const DecodeArgs& a, Cursor c, int 
 // Stream: K/V tiles read with non-temporal loads (a template parameter, not a
 // runtime branch: the compiler would merge two loads of one address and drop the
 // hint).
-template <class Path, typename T, int D, int NW, bool Stream>
+template <class Path, typename T, int D, int NW, bool Stream, bool Step>
 __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     constexpr int NL = Path::NL;
     const int lane = threadIdx.x & (kWave - 1);
+    if constexpr (Step) {
+        // The step's metadata, written by workgroup 0: every sequence's context length,
+        // the table entry of its new token's block, and the blocks its last block's
+        // tiles are read from and written to.  The flag is released after those
+        // writes and every workgroup acquires it before reading any of them.
+        // Workgroups are dispatched in index order, so workgroup 0 is resident before
+        // any workgroup that waits for it.  The wait is bounded all the same: one that
+        // runs past its limit is counted in sync[2] and the workgroup goes on (its
+        // results are then unspecified, but every access stays in bounds).  The last
+        // workgroup past the flag resets it for the next call.
+        if (blockIdx.x == 0) {
+            const int B = a.block_size;
+            const int cap = a.max_blocks * B;
+            for (int i = static_cast<int>(threadIdx.x); i < a.num_seqs; i += 64 * NW) {
+                // requested together: these may live in host memory
+                const int len_in = a.lens_in[i];
+                const int64_t slot = a.new_slots[i];
+                const int cs = a.cow_in ? a.cow_in[2 * i] : -1;
+                const int cd = a.cow_in ? a.cow_in[2 * i + 1] : -1;
+                const int len = min(max(len_in, 0), cap);
+                int rb = 0, wb = 0, flags = 0;
+                if (len > 0 && slot >= 0 && slot < static_cast<int64_t>(a.num_blocks) * B &&
+                    static_cast<int>(slot % B) == (len - 1) % B) {
+                    const int blk = static_cast<int>(slot / B);
+                    const bool cow = cs >= 0 && cs < a.num_blocks && cd == blk && cs != cd;
+                    rb = cow ? cs : blk;
+                    wb = blk;
+                    flags = 1 | (cow ? 2 : 0);
+                    a.tables_dev[static_cast<size_t>(i) * a.max_blocks + (len - 1) / B] = blk;
+                }
+                a.lens_dev[i] = len_in;
+                *reinterpret_cast<u32x4*>(a.seq_info + 4 * i) =
+                    u32x4{static_cast<unsigned>(rb), static_cast<unsigned>(wb),
+                          static_cast<unsigned>(flags), 0u};
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_store(a.sync, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // While it waits, every workgroup writes its share of the step's new tokens into
+        // their slots (the scatter of the two-call form).  Nothing in this launch reads
+        // those bytes: the waves that fold a token's tile take the token from k_new /
+        // v_new themselves.  Written now, before the K/V streaming starts, the stores
+        // do not compete with it.
+        {
+            constexpr int X = 16 / static_cast<int>(sizeof(T));
+            constexpr int E = X / 4;
+            const int G = static_cast<int>(gridDim.x);
+            const int B = a.block_size;
+            const int tpb = a.tiles_per_block;
+            const int Hkv = a.num_kv_heads;
+            const int cap = a.max_blocks * B;
+            const int t_lo = static_cast<int>(static_cast<long long>(a.num_seqs) * blockIdx.x / G);
+            const int t_hi = static_cast<int>(static_cast<long long>(a.num_seqs) * (blockIdx.x + 1) / G);
+            const int work = (t_hi - t_lo) * Hkv * D;
+            T* kwr = static_cast<T*>(const_cast<void*>(a.k_cache));
+            T* vwr = static_cast<T*>(const_cast<void*>(a.v_cache));
+            for (int w = static_cast<int>(threadIdx.x); w < work; w += 64 * NW) {
+                const int pair = w / D, d = w - pair * D;
+                const int t = t_lo + pair / Hkv, h = pair - (pair / Hkv) * Hkv;
+                const int len = min(max(a.lens_in[t], 0), cap);
+                const int64_t slot = a.new_slots[t];
+                if (len <= 0 || slot < 0 || slot >= static_cast<int64_t>(a.num_blocks) * B ||
+                    static_cast<int>(slot % B) != (len - 1) % B)
+                    continue;
+                const int64_t blk = slot / B;
+                const int o = static_cast<int>(slot - blk * B);
+                const int ti = o & 15, j = ti >> 2, r = ti & 3;
+                const size_t tile_base = ((static_cast<size_t>(blk) * tpb + (o >> 4)) * Hkv + h) * (kTile * D);
+                const size_t src = (static_cast<size_t>(t) * Hkv + h) * D;
+                const int m = d / (16 * E), ee = (d >> 4) % E, i = d & 15;
+                vwr[tile_base + ((((m * 4 + j) * 16 + i) * E + ee) * 4 + r)] =
+                    static_cast<const T*>(a.v_new)[src + d];
+                if (d % X == 0)
+                    *reinterpret_cast<u32x4*>(kwr + tile_base + ((d / X) * 16 + ti) * X) =
+                        *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.k_new) + src + d);
+            }
+        }
+        if (threadIdx.x == 0) {
+            int spins = 0;
+            while (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins > kStepSpinLimit) {
+                    __hip_atomic_fetch_add(a.sync + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+            const int past = __hip_atomic_fetch_add(a.sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (past == static_cast<int>(gridDim.x) - 1) {
+                __hip_atomic_store(a.sync + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        // One agent-scope acquire per workgroup: it invalidates this CU's and this
+        // XCD's caches, and the barrier orders the other waves' reads after it.
+        if (threadIdx.x < kWave) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();
+    }
     const int S = a.num_seqs;
     const int W = a.num_units;
     const int R = a.rows;
@@ -769,7 +973,7 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
 
     // ---- fetch side: chunk, next lane of it, tiles issued so far
-    Chunk ch = build_chunk<Path>(a, Cursor{row0, uni(seq0), uni(t00)}, n_tiles, lane);
+    Chunk ch = build_chunk<Path, Step>(a, Cursor{row0, uni(seq0), uni(t00)}, n_tiles, lane);
     int kf = 0, fetched = 0;
     int f_seq = -1, f_row = -1;  // piece of the last fetched tile
     typename Path::Q q, qn;
@@ -778,8 +982,11 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         u32x4 k[NL], v[NL];
         TileRef r;
         bool opens;  // first tile of a piece
+        TokenV<T, NL> tok;    // decode step: the new token's V values, when the tile holds its place
+        bool pend;            // decode step: the tile's write-back is still to be stored
     };
     Buf A, B;
+    A.pend = B.pend = false;
 
     // A split sequence's pieces sit in units us .. ue (in unit us in record slot 1,
     // elsewhere in slot 0).  With the merge folded in (a.fused), each holder
@@ -801,6 +1008,50 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         arrive_first = false;
     };
+    // Decode step: a tile of a sequence's last block takes the new token at its place
+    // (fixup, before the tile is folded).  When the block is copied (copy-on-write) the
+    // whole tile is written to the copy, and the wave holding the token's tile also
+    // copies the block's tiles after it; a block written in place needs nothing more
+    // (the token itself was scattered at the start).  The write-back (flush) waits
+    // until the buffer is reused, right after the next wait for loads, so that its
+    // stores complete alongside the next tile's loads.
+    u32x4* const kw = const_cast<u32x4*>(static_cast<const u32x4*>(a.k_cache));
+    u32x4* const vw = const_cast<u32x4*>(static_cast<const u32x4*>(a.v_cache));
+    auto flush = [&](Buf& b) {
+        if constexpr (Step) {
+            if (!b.pend) return;
+            b.pend = false;
+            const int p = b.r.ptok;
+            const size_t wo = static_cast<size_t>(b.r.wtoff) * Path::TILE_U4;
+#pragma unroll
+            for (int s = 0; s < NL; ++s) kw[wo + lane + s * kWave] = b.k[s];
+#pragma unroll
+            for (int s = 0; s < NL; ++s) vw[wo + lane + s * kWave] = b.v[s];
+            if (p >= 0) {
+                const int tpb = a.tiles_per_block;
+                const int tib = b.r.tile % tpb;
+                for (int tt = tib + 1; tt < tpb; ++tt) {
+                    const size_t so = static_cast<size_t>(b.r.toff + (tt - tib) * a.num_kv_heads) * Path::TILE_U4;
+                    const size_t dof = static_cast<size_t>(b.r.wtoff + (tt - tib) * a.num_kv_heads) * Path::TILE_U4;
+                    // a rare path (the tiles past the token of a copied block): one group at a time
+#pragma unroll 1
+                    for (int s = 0; s < NL; ++s) {
+                        const u32x4 ck = kc[so + lane + s * kWave];
+                        const u32x4 cv = vc[so + lane + s * kWave];
+                        kw[dof + lane + s * kWave] = ck;
+                        vw[dof + lane + s * kWave] = cv;
+                    }
+                }
+            }
+        }
+    };
+    auto fixup = [&](Buf& b) {
+        if constexpr (Step) {
+            if (b.r.wtoff < 0) return;
+            if (b.r.ptok >= 0) patch_token_v<T, NL>(b.v, b.tok, b.r.ptok, lane);
+            b.pend = b.r.wtoff != b.r.toff;  // copy-on-write: the tile goes to the copy
+        }
+    };
     auto issue = [&](Buf& b) {
         // One tile in flight per wave: the previous tile's loads have all returned
         // before the next tile is requested.  Measured on MI355X, this sustains more
@@ -808,6 +1059,9 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         // lengthen the memory queues); the unit count then sets the bytes in flight.
         wait_all_loads();
         if (arrive_first) arrive();
+        // Decode step: this buffer's write-back goes out now, beside the next tile's
+        // loads, so that no wait is spent on it alone.
+        if constexpr (Step) flush(b);
         // The rows of a workgroup walk the same tiles; meeting once per tile keeps
         // their requests for one block's adjacent heads (consecutive 4 KiB pieces of
         // K and of V) reaching memory together.  Measured with streamed loads, that
@@ -822,13 +1076,14 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
                 // changed under the kernel: fold harmless in-pool tiles instead of spinning.
                 ch.n = 1;
                 ch.seq = ch.tile = ch.row = ch.ctx = ch.toff = 0;
+                ch.wtoff = ch.ptok = -1;
                 kf = 0;
                 break;
             }
-            ch = build_chunk<Path>(a, ch.next, n_tiles - fetched, lane);
+            ch = build_chunk<Path, Step>(a, ch.next, n_tiles - fetched, lane);
             kf = 0;
         }
-        b.r = tile_ref(ch, kf);
+        b.r = tile_ref<Step>(ch, kf);
         ++kf;
         ++fetched;
         // The query of a new piece is requested before the tile, so that waiting
@@ -845,6 +1100,35 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         const size_t off = static_cast<size_t>(b.r.toff) * Path::TILE_U4;
         const u32x4* kt = kc + off;
         const u32x4* vt = vc + off;
+        if constexpr (Step) {
+            // Every lane reads its V values of the new token (harmless ones when it has
+            // none), so the loads in flight never depend on the tile.
+            const size_t ro = (static_cast<size_t>(b.r.seq) * a.num_kv_heads +
+                               Path::kv_head(a, b.r.row)) * D;
+            const T* vnew = static_cast<const T*>(a.v_new);
+            load_token_v<T, NL>(b.tok, vnew + ro, vnew, b.r.ptok, lane);
+            if (b.r.ptok >= 0) {
+                // The new token's tile: this launch has already written the token into
+                // it (the scatter at the start), and non-temporal loads of lines written
+                // in the same launch were measured to cost ~17 us per step on the
+                // batch-256 config, so this tile is read with ordinary loads.  The lanes
+                // holding the token's place read its K groups from the new row instead
+                // (the scatter's bytes may sit in another XCD's cache).
+                constexpr int X = TokenV<T, NL>::X;
+                const T* krow = static_cast<const T*>(a.k_new) + ro + (lane >> 4) * X;
+                const bool mine = (lane & 15) == b.r.ptok;
+                const u32x4* kp = mine ? reinterpret_cast<const u32x4*>(krow) : kt + lane;
+                const int ks = mine ? 4 * X * static_cast<int>(sizeof(T)) / 16 : kWave;
+#pragma unroll
+                for (int s = 0; s < NL; ++s) b.k[s] = kp[s * ks];
+                const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<u32x4*>(vt), static_cast<short>(0), Path::TILE_U4 * 16, kBufferRsrcWord3);
+#pragma unroll
+                for (int s = 0; s < NL; ++s)
+                    b.v[s] = __builtin_amdgcn_raw_buffer_load_b128(vr, (lane + s * kWave) * 16, 0, 0);
+                return;
+            }
+        }
         if constexpr (!Stream) {
 #pragma unroll
             for (int s = 0; s < NL; ++s) b.k[s] = kt[lane + s * kWave];
@@ -857,6 +1141,7 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
             for (int s = 0; s < NL; ++s) b.v[s] = __builtin_nontemporal_load(vt + lane + s * kWave);
         }
     };
+
 
     // ---- compute side: the open piece
     typename Path::Acc st;
@@ -941,20 +1226,27 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     for (; g + 2 < n_tiles; g += 2) {
         enter(A, g);
         issue(B);
+        fixup(A);
         Path::tile(a, st, q, A.k, A.v, A.r.tile, A.r.ctx, lane);
         enter(B, g + 1);
         issue(A);
+        fixup(B);
         Path::tile(a, st, q, B.k, B.v, B.r.tile, B.r.ctx, lane);
     }
     enter(A, g);
     if (g + 1 < n_tiles) {
         issue(B);
+        fixup(A);
         Path::tile(a, st, q, A.k, A.v, A.r.tile, A.r.ctx, lane);
         enter(B, g + 1);
+        fixup(B);
         Path::tile(a, st, q, B.k, B.v, B.r.tile, B.r.ctx, lane);
     } else {
+        fixup(A);
         Path::tile(a, st, q, A.k, A.v, A.r.tile, A.r.ctx, lane);
     }
+    flush(A);
+    flush(B);
     if (arrive_first) {
         wait_all_loads();
         arrive();
@@ -996,25 +1288,39 @@ hipError_t launch_pass2(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <class Path, typename T, int D, bool Stream>
+template <class Path, typename T, int D, int NW, bool Stream, bool Step>
+hipError_t launch_pass1_nw(const DecodeArgs& a, int groups, hipStream_t st) {
+    // (a cooperative launch would guarantee residency outright, but measured ~15 us
+    // slower per launch on this part; dispatch in index order is what the step's
+    // wait relies on)
+    hipLaunchKernelGGL((decode_pass1<Path, T, D, NW, Stream, Step>), dim3(groups), dim3(NW * kWave), 0, st, a);
+    return hipSuccess;
+}
+
+template <class Path, typename T, int D, bool Stream, bool Step>
 hipError_t launch_pass1(const DecodeArgs& a, int nw, int groups, hipStream_t st) {
     switch (nw) {
-        case 1: hipLaunchKernelGGL((decode_pass1<Path, T, D, 1, Stream>), dim3(groups), dim3(kWave), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((decode_pass1<Path, T, D, 2, Stream>), dim3(groups), dim3(2 * kWave), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((decode_pass1<Path, T, D, 4, Stream>), dim3(groups), dim3(4 * kWave), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((decode_pass1<Path, T, D, 8, Stream>), dim3(groups), dim3(8 * kWave), 0, st, a); break;
+        case 1: return launch_pass1_nw<Path, T, D, 1, Stream, Step>(a, groups, st);
+        case 2: return launch_pass1_nw<Path, T, D, 2, Stream, Step>(a, groups, st);
+        case 4: return launch_pass1_nw<Path, T, D, 4, Stream, Step>(a, groups, st);
+        case 8: return launch_pass1_nw<Path, T, D, 8, Stream, Step>(a, groups, st);
         default: return hipErrorInvalidValue;
     }
-    return hipSuccess;
 }
 
 template <class Path, typename T, int D>
 hipError_t launch_two_pass(const DecodeArgs& a, int passes, hipStream_t st) {
+    const int nw = a.waves_per_group;
+    const int groups = nw > 1 ? (a.num_units / a.rows) * a.rows / nw : a.num_units;
+    if (passes & 4) {  // the decode step: one launch with the step's writes, merge folded in
+        const hipError_t e0 = a.keep_cached ? launch_pass1<Path, T, D, false, true>(a, nw, groups, st)
+                                            : launch_pass1<Path, T, D, true, true>(a, nw, groups, st);
+        if (e0 != hipSuccess) return e0;
+        return hipGetLastError();
+    }
     if (passes & 1) {
-        const int nw = a.waves_per_group;
-        const int groups = nw > 1 ? (a.num_units / a.rows) * a.rows / nw : a.num_units;
-        const hipError_t e0 = a.keep_cached ? launch_pass1<Path, T, D, false>(a, nw, groups, st)
-                                            : launch_pass1<Path, T, D, true>(a, nw, groups, st);
+        const hipError_t e0 = a.keep_cached ? launch_pass1<Path, T, D, false, false>(a, nw, groups, st)
+                                            : launch_pass1<Path, T, D, true, false>(a, nw, groups, st);
         if (e0 != hipSuccess) return e0;
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1038,6 +1344,12 @@ hipError_t launch_group(const DecodeArgs& a, int passes, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_decode_step(int dtype, int head_dim, bool use_group_kernel, const DecodeArgs& a,
+                              hipStream_t stream) {
+    return launch_decode(dtype, head_dim, use_group_kernel, a, 4, stream);
+}
+
 
 hipError_t launch_decode(int dtype, int head_dim, bool use_group_kernel, const DecodeArgs& a,
                          int passes, hipStream_t stream) {

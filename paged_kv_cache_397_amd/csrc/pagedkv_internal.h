@@ -37,6 +37,22 @@ struct DecodeArgs {
     int32_t fused;              // 1: pass 1 merges split sequences itself (no pass 2)
     int32_t keep_cached;        // 1: K/V tiles read with ordinary loads (kept in L2 / MALL)
     float scale_log2e;          // scale * log2(e): scores are kept in base-2 units
+    // Decode step (pa_decode_step): the step's writes are folded into the launch.
+    // Workgroup 0 first copies lens_in into context_lens, sets each sequence's table
+    // entry for the block of its new token and fills seq_info; every workgroup waits
+    // for that (sync[0]) before reading any of them.  Waves reading a tile of a
+    // sequence's last block take its new token from k_new / v_new and write it (and
+    // a copy-on-write copy) to the cache.
+    const int32_t* lens_in;     // [S] context lengths including the step's token (host or device)
+    const int64_t* new_slots;   // [S] slot of sequence i's new token (position lens_in[i] - 1), -1 = none
+    const int32_t* cow_in;      // [S][2] (src, dst) copy-on-write pair of sequence i, or NULL
+    const void* k_new;          // [S, Hkv, D] the step's new keys and values
+    const void* v_new;
+    int32_t* lens_dev;          // context_lens, written by workgroup 0
+    int32_t* tables_dev;        // block_tables, written by workgroup 0
+    int32_t* seq_info;          // [S][4]: read block, write block of the last block; flags
+    int32_t* sync;              // [4]: released flag, workgroups past it, spin time-outs
+    int32_t block_size;
 };
 
 // Everything the chunked-prefill kernel needs; passed by value.
@@ -61,6 +77,10 @@ struct PrefillArgs {
 };
 
 constexpr int kRecInts = 8;  // per-unit record: row, seq, first unit, last unit of the split ending there
+// Decode step: polls of the metadata flag before a workgroup gives up waiting (each
+// poll sleeps ~128 clocks, so about 0.1 s): only a launch whose workgroup 0 never
+// ran could reach it.
+constexpr int kStepSpinLimit = 1 << 20;
 // Aligned split: a sequence with n tiles costs kTileCost n + kPieceCost.  Measured on
 // the batch-256 GQA workload, a unit's time grows by about 0.8 of a tile per extra
 // sequence (piece) in its range, so a piece is charged one tile.
@@ -98,5 +118,9 @@ hipError_t launch_prefill(int head_dim, int group, int max_query_len, PrefillArg
                           hipStream_t stream);
 hipError_t launch_decode(int dtype, int head_dim, bool use_group_kernel, const DecodeArgs& a,
                          int passes, hipStream_t stream);
+// One decode step with its cache writes folded in (the single-kernel decode with
+// DecodeArgs' step fields set).
+hipError_t launch_decode_step(int dtype, int head_dim, bool use_group_kernel, const DecodeArgs& a,
+                              hipStream_t stream);
 
 }  // namespace pkv

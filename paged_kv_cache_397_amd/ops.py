@@ -149,9 +149,10 @@ def _append_args(spec, k, v, slot_mapping, k_cache, v_cache, cow_pairs, block_ta
 def append_tokens(spec: CacheSpec, k, v, slot_mapping, k_cache, v_cache, cow_pairs=None,
                   block_tables=None, table_updates=None, lens_in=None, lens_out=None,
                   stream=None):
-    """One launch for a decode step's writes: copy-on-write copies (cow_pairs [T, 2],
-    row t for token t, -1 = none), table updates ([n, 3] rows (row, column, block)),
-    the scatter of k[t], v[t] ([T, Hkv, D]) into slot_mapping[t], and lens_out[:] =
+    """A decode step's writes: copy-on-write copies (cow_pairs [T, 2], row t for
+    token t, -1 = none; they run as a launch of their own first, so pass None when
+    the step copies nothing), table updates ([n, 3] rows (row, column, block)), the
+    scatter of k[t], v[t] ([T, Hkv, D]) into slot_mapping[t], and lens_out[:] =
     lens_in.  slot_mapping, cow_pairs, table_updates and lens_in may be pinned host
     tensors."""
     args = _append_args(spec, k, v, slot_mapping, k_cache, v_cache, cow_pairs, block_tables,
@@ -239,6 +240,75 @@ def paged_attn_decode_merge(spec: CacheSpec, out, q, k_cache, v_cache, block_tab
         raise ValueError("the partial/merge split needs an explicit shared workspace")
     return _decode("pa_paged_attn_decode_merge", spec, out, q, k_cache, v_cache, block_tables,
                    context_lens, scale, num_units, workspace, stream, keep_cached)
+
+
+def decode_step_workspace(spec: CacheSpec, num_q_heads: int, num_seqs: int, num_units: int = 0,
+                          device="cuda"):
+    """Zero-filled workspace of a decode step (it also serves paged_attn_decode)."""
+    n = int(N.lib().pa_decode_step_workspace_bytes(ctypes.byref(spec.desc()), num_q_heads,
+                                                   num_units, num_seqs))
+    if n == 0:
+        raise N.PagedKVError(N.PA_ERR_INVALID_ARG, "pa_decode_step_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _step_args(spec, out, q, k_new, v_new, slot_mapping, cow_pairs, lens_in, k_cache, v_cache,
+               block_tables, context_lens, scale, num_units, workspace, stream, keep_cached):
+    S, Hq, D = q.shape
+    if D != spec.head_dim or tuple(out.shape) != (S, Hq, D):
+        raise ValueError("q and out must be [S, Hq, D]")
+    if tuple(k_new.shape) != (S, spec.num_kv_heads, D) or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must be [S, Hkv, D]")
+    if slot_mapping.numel() != S or lens_in.numel() != S or context_lens.numel() != S:
+        raise ValueError("slot_mapping, lens_in and context_lens must hold one entry per sequence")
+    if cow_pairs is not None and cow_pairs.numel() != 2 * S:
+        raise ValueError("cow_pairs must be [S, 2]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, maxB]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    desc = spec.desc()
+    return desc, (
+        ctypes.byref(desc), _dev(out, "out", spec.torch_dtype), _dev(q, "q", spec.torch_dtype),
+        _dev(k_new, "k_new", spec.torch_dtype), _dev(v_new, "v_new", spec.torch_dtype),
+        _acc(slot_mapping, "slot_mapping", torch.int64),
+        None if cow_pairs is None else _acc(cow_pairs, "cow_pairs", torch.int32),
+        _acc(lens_in, "lens_in", torch.int32), _dev(k_cache, "k_cache", spec.torch_dtype),
+        _dev(v_cache, "v_cache", spec.torch_dtype),
+        _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, block_tables.shape[1],
+        ctypes.c_float(scale), int(num_units), _dev(workspace, "workspace"), workspace.numel(),
+        DECODE_KEEP_CACHED if keep_cached else 0, _stream(stream))
+
+
+def decode_step(spec: CacheSpec, out, q, k_new, v_new, slot_mapping, lens_in, k_cache, v_cache,
+                block_tables, context_lens, cow_pairs=None, scale: float | None = None,
+                num_units: int = 0, workspace=None, stream=None, keep_cached: bool = False):
+    """One decode step in one launch: sequence i's new token (k_new[i], v_new[i]) is
+    written at slot_mapping[i] (after the copy cow_pairs[i], if any), block_tables and
+    context_lens are updated for it (context_lens = lens_in), and out is decode
+    attention over every cached token, the new ones included.  slot_mapping,
+    cow_pairs and lens_in may be pinned host tensors."""
+    if workspace is None:
+        workspace = decode_step_workspace(spec, q.shape[1], q.shape[0], num_units, q.device)
+    _, args = _step_args(spec, out, q, k_new, v_new, slot_mapping, cow_pairs, lens_in, k_cache,
+                         v_cache, block_tables, context_lens, scale, num_units, workspace, stream,
+                         keep_cached)
+    N.check(N.lib().pa_decode_step(*args), "pa_decode_step")
+    return out
+
+
+def bind_decode_step(spec: CacheSpec, out, q, k_new, v_new, slot_mapping, lens_in, k_cache,
+                     v_cache, block_tables, context_lens, cow_pairs=None,
+                     scale: float | None = None, num_units: int = 0, workspace=None, stream=None,
+                     keep_cached: bool = False) -> "BoundCall":
+    """decode_step with its arguments fixed (same meaning as decode_step)."""
+    if workspace is None:
+        raise ValueError("a bound decode step needs an explicit workspace")
+    desc, args = _step_args(spec, out, q, k_new, v_new, slot_mapping, cow_pairs, lens_in, k_cache,
+                            v_cache, block_tables, context_lens, scale, num_units, workspace,
+                            stream, keep_cached)
+    return BoundCall("pa_decode_step", args, keep=desc)
 
 
 def paged_attn_decode_noalloc(spec: CacheSpec, out, q, k_cache, v_cache, block_tables,

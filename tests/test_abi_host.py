@@ -140,3 +140,22 @@ def test_prefill_argument_checks_without_a_gpu():
     assert lib.pa_paged_attn_prefill(*args(bf16, 4, mql=-1)) == N.PA_ERR_INVALID_ARG
     assert lib.pa_paged_attn_prefill(*args(bf16, 4, T=0)) == N.PA_OK  # nothing to do
     assert lib.pa_paged_attn_prefill(*args(bf16, 4)) == N.PA_ERR_INVALID_ARG  # null pointers
+
+
+def test_probe_library_exports_its_declared_function():
+    """The read-bandwidth probe (include/pagedkv_probe.h) is a library of its own;
+    it loads without a GPU and rejects bad arguments before any launch."""
+    from paged_kv_cache_397_amd import build as B
+    src = open(os.path.join(ROOT, "include", "pagedkv_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    declared = sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src)))
+    assert declared == ["pa_probe_gather_read"]
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    fn = lib.pa_probe_gather_read
+    fn.restype = ctypes.c_int32
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_void_p]
+    assert fn(None, FAKE, 4, FAKE, 1, 1, FAKE, 1, 1, None) == 1          # null buffer
+    assert fn(FAKE, FAKE, 4, FAKE, 1, 1, FAKE, 1, 3, None) == 1          # tiles in flight not 1 or 2
+    assert fn(FAKE + 4, FAKE, 4, FAKE, 1, 1, FAKE, 1, 1, None) == 1      # misaligned

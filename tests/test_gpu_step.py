@@ -1,0 +1,198 @@
+"""GPU: the decode step in one launch (pa_decode_step) against the same step as two
+calls (pa_append_tokens, then pa_paged_attn_decode) and against the fp64 oracle.
+
+The step writes each sequence's new token (and, for a sequence whose last block is
+shared, its copy-on-write copy) with the waves that read the token's tile, updates
+the table entry and the context lengths, and attends in the same launch.  Over
+several consecutive steps, outputs must equal the two-call path bit for bit, and so
+must every byte of both caches, the tables and the lengths; outputs must match the
+oracle on the logical data."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import contiguous_decode
+from oracle.layout import to_float64
+from paged_kv_cache_397_amd import ops
+from paged_kv_cache_397_amd.batch import PagedKVCache, to_device, to_storage
+from tests.gpu_util import assert_close, parallel_map
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return bool(torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                            b.view(torch.uint8) if b.dtype != torch.int32 else b))
+
+
+def _run(dtype, D, B, Hq, Hkv, units, seed, steps=3, forked=True, skip_some=True, pinned=False,
+         check_oracle=True):
+    N = 1024
+    spec = ops.CacheSpec(num_blocks=N, block_size=B, num_kv_heads=Hkv, head_dim=D, dtype=dtype)
+    cache = PagedKVCache(spec, gen.pool_permutation(seed, N), fill=float("nan"))
+    rng = gen.stream(seed, 77)
+    logical = {}
+    seqs = []
+    # private sequences of assorted lengths (some end exactly at a block boundary)
+    for i, L in enumerate([1, 15, 16, B, B + 1, 3 * B - 1, 200, 37]):
+        K, V = gen.seq_kv(seed, i, L, Hkv, D, dtype)
+        cache.add_sequence(i, K, V)
+        logical[i] = [K, V]
+        seqs.append(i)
+    if forked:
+        # a parent whose last block is shared and partly full, and three children:
+        # their first appends copy it (the last sharer writes in place); a second
+        # family whose shared partial block holds its token in a later tile
+        for base, L in ((100, B + B // 2 + 3), (200, 2 * B + 5)):
+            K, V = gen.seq_kv(seed, base, L, Hkv, D, dtype)
+            cache.add_sequence(base, K, V)
+            logical[base] = [K, V]
+            seqs.append(base)
+            for c in (1, 2, 3):
+                cache.alloc.fork(base, base + c)
+                logical[base + c] = [K.copy(), V.copy()]
+                seqs.append(base + c)
+    S = len(seqs)
+    maxb = -(-(3 * B + 200 + steps + 8) // B)
+    tables_h, ctx_h = cache.alloc.batch_metadata(seqs, maxb)
+    # path A: two calls; path B: the one-launch step, on a copy of the same state
+    kA, vA = cache.k, cache.v
+    kB, vB = kA.clone(), vA.clone()
+    tA, tB = torch.from_numpy(tables_h.copy()).cuda(), torch.from_numpy(tables_h.copy()).cuda()
+    cA = torch.from_numpy(ctx_h.copy()).cuda()
+    cB = cA.clone()
+    wsA = ops.decode_workspace(spec, Hq, units)
+    wsB = ops.decode_step_workspace(spec, Hq, S, units)
+    scale = 1 / math.sqrt(D)
+    lens = ctx_h.astype(np.int64).copy()
+    n_cow = 0
+    host = (lambda a: torch.from_numpy(np.ascontiguousarray(a)).pin_memory()) if pinned else \
+           (lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    for n in range(steps):
+        # which sequences append a token this step (the others are attended as cached)
+        active = np.ones(S, dtype=bool)
+        if skip_some and n == 1:
+            active[[1, 4]] = False
+        ids = np.array(seqs, dtype=np.int64)[active]
+        st, done, slots_a, cows_a, nb, nc = cache.alloc.append_batch(ids)
+        assert st == 0 and done == len(ids)
+        slots = np.full(S, -1, dtype=np.int64)
+        slots[active] = slots_a
+        cows = np.full((S, 2), -1, dtype=np.int32)
+        cows[active] = cows_a
+        n_cow += int((cows[:, 0] >= 0).sum())
+        lens[active] += 1
+        rows = np.nonzero(nb >= 0)[0]
+        updates = np.stack([np.nonzero(active)[0][rows], nc[rows], nb[rows]], 1).astype(np.int32)
+        kn = gen.draw_values(rng, (S, Hkv, D), dtype)
+        vn = gen.draw_values(rng, (S, Hkv, D), dtype)
+        q_host = gen.draw_values(rng, (S, Hq, D), dtype)
+        for k, s in enumerate(seqs):
+            if active[k]:
+                logical[s][0] = np.concatenate([logical[s][0], kn[k:k + 1]])
+                logical[s][1] = np.concatenate([logical[s][1], vn[k:k + 1]])
+        knd, vnd, q = to_device(kn, spec), to_device(vn, spec), to_device(q_host, spec)
+        lens32 = lens.astype(np.int32)
+        any_cow = bool((cows[:, 0] >= 0).any())
+        # path A
+        ops.append_tokens(spec, knd[torch.from_numpy(np.nonzero(active)[0]).cuda()].contiguous(),
+                          vnd[torch.from_numpy(np.nonzero(active)[0]).cuda()].contiguous(),
+                          torch.from_numpy(slots_a).cuda(), kA, vA,
+                          cow_pairs=torch.from_numpy(np.ascontiguousarray(cows_a)).cuda() if any_cow else None,
+                          block_tables=tA, table_updates=torch.from_numpy(updates).cuda(),
+                          lens_in=torch.from_numpy(lens32).cuda(), lens_out=cA)
+        outA = torch.full((S, Hq, D), float("nan"), dtype=spec.torch_dtype, device="cuda")
+        ops.paged_attn_decode(spec, outA, q, kA, vA, tA, cA, scale, units, wsA)
+        # path B
+        outB = torch.full_like(outA, float("nan"))
+        ops.decode_step(spec, outB, q, knd, vnd, host(slots), host(lens32), kB, vB, tB, cB,
+                        cow_pairs=host(cows) if any_cow else None, scale=scale, num_units=units,
+                        workspace=wsB)
+        torch.cuda.synchronize()
+        what = f"{dtype} D{D} B{B} G{Hq // Hkv} units {units} step {n}"
+        assert _same(outA, outB), what + ": outputs differ"
+        assert _same(kA, kB) and _same(vA, vB), what + ": cache bytes differ"
+        assert torch.equal(tA, tB) and torch.equal(cA, cB), what + ": tables or lengths differ"
+        assert int(wsB[-4 * max(units, 1):].count_nonzero()) == 0 if units else True
+        if check_oracle:
+            got = to_float64(to_storage(outB), dtype)
+            ref = np.stack(parallel_map(
+                lambda k: contiguous_decode(q_host[k], *logical[seqs[k]], scale, dtype), range(S)))
+            assert_close(got, ref, dtype, what + " vs oracle")
+    if forked:
+        assert n_cow == 6, n_cow
+    return n_cow
+
+
+@pytest.mark.parametrize("dtype,D,B,Hq,Hkv", [
+    ("bf16", 128, 16, 32, 8),    # group path, G = 4 (the headline shape)
+    ("bf16", 128, 16, 8, 8),     # per-head path
+    ("bf16", 64, 32, 8, 4),      # group, G = 2, two tiles per block
+    ("bf16", 128, 64, 16, 2),    # group, G = 8, four tiles per block
+    ("f32", 64, 16, 4, 2),       # fp32 per-head path, two rows per KV head
+    ("f32", 128, 32, 2, 2),
+])
+@pytest.mark.parametrize("units", [0, 7, 40])
+def test_step_equals_append_then_decode(dtype, D, B, Hq, Hkv, units):
+    _run(dtype, D, B, Hq, Hkv, units, seed=300 + D + B + Hq + units)
+
+
+def test_step_with_metadata_in_pinned_host_memory():
+    _run("bf16", 128, 16, 32, 8, 0, seed=401, pinned=True)
+
+
+def test_step_at_the_batch_256_gqa_shape():
+    """The headline shape (256 sequences, 32 q / 8 kv heads, log-uniform lengths) for
+    a few steps at the default units: equal to the two calls, and to the oracle."""
+    spec = ops.CacheSpec(num_blocks=40000, block_size=16, num_kv_heads=8, head_dim=128,
+                         dtype="bf16")
+    rng = gen.stream(402, 1)
+    ctx = np.clip(np.rint(np.exp(rng.uniform(np.log(16), np.log(4096), 256))), 16, 4096).astype(np.int64)
+    cache = PagedKVCache(spec, gen.pool_permutation(403, spec.num_blocks), fill=float("nan"))
+    logical = {}
+    for i, L in enumerate(ctx):
+        K, V = gen.seq_kv(404, i, int(L), 8, 128, "bf16")
+        cache.add_sequence(i, K, V)
+        logical[i] = [K, V]
+    S, maxb = 256, 4096 // 16 + 4
+    tables_h, ctx_h = cache.alloc.batch_metadata(range(S), maxb)
+    kA, vA = cache.k, cache.v
+    kB, vB = kA.clone(), vA.clone()
+    tA, tB = torch.from_numpy(tables_h.copy()).cuda(), torch.from_numpy(tables_h.copy()).cuda()
+    cA = torch.from_numpy(ctx_h.copy()).cuda()
+    cB = cA.clone()
+    wsA = ops.decode_workspace(spec, 32, 0)
+    wsB = ops.decode_step_workspace(spec, 32, S, 0)
+    lens = ctx_h.astype(np.int64).copy()
+    for n in range(3):
+        st, done, slots, cows, nb, nc = cache.alloc.append_batch(np.arange(S))
+        assert st == 0 and (cows < 0).all()
+        lens += 1
+        rows = np.nonzero(nb >= 0)[0]
+        updates = np.stack([rows, nc[rows], nb[rows]], 1).astype(np.int32)
+        kn, vn = gen.new_tokens(405, n, S, 8, 128, "bf16")
+        q_host = gen.q_values(405, n, S, 32, 128, "bf16")
+        for i in range(S):
+            logical[i][0] = np.concatenate([logical[i][0], kn[i:i + 1]])
+            logical[i][1] = np.concatenate([logical[i][1], vn[i:i + 1]])
+        knd, vnd, q = to_device(kn, spec), to_device(vn, spec), to_device(q_host, spec)
+        lens32 = torch.from_numpy(lens.astype(np.int32))
+        ops.append_tokens(spec, knd, vnd, torch.from_numpy(slots).cuda(), kA, vA, block_tables=tA,
+                          table_updates=torch.from_numpy(updates).cuda(), lens_in=lens32.cuda(),
+                          lens_out=cA)
+        outA = torch.full((S, 32, 128), float("nan"), dtype=spec.torch_dtype, device="cuda")
+        ops.paged_attn_decode(spec, outA, q, kA, vA, tA, cA, None, 0, wsA)
+        outB = torch.full_like(outA, float("nan"))
+        ops.decode_step(spec, outB, q, knd, vnd, torch.from_numpy(slots).pin_memory(),
+                        lens32.pin_memory(), kB, vB, tB, cB, num_units=0, workspace=wsB)
+        torch.cuda.synchronize()
+        assert _same(outA, outB), n
+        assert _same(kA, kB) and _same(vA, vB) and torch.equal(tA, tB) and torch.equal(cA, cB), n
+    got = to_float64(to_storage(outB), "bf16")
+    ref = np.stack(parallel_map(
+        lambda i: contiguous_decode(q_host[i], *logical[i], 1 / math.sqrt(128), "bf16"), range(S)))
+    assert_close(got, ref, "bf16", "gqa step vs oracle")
