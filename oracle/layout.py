@@ -8,9 +8,10 @@ section 2.2; hihuo.com "vLLM 原理：PagedAttention 和 Continuous Batching",
 section PagedAttention > 工作原理 > 1. 页表管理).  The byte layout inside a block
 is this library's own contract, stated in ``include/pagedkv.h``:
 
-* a block of B tokens is cut into B/16 tiles of 16 tokens;
-* K tile   = [D/X][16][X]          (X = 16 bytes / element size)
-* V tile   = [D/(16E)][4][16][E][4] (E = X/4): each 16-byte group holds four
+* a block of B tokens is cut into B/TT tiles of TT = min(B, 16) tokens (a block
+  of 8 tokens is one tile of 8);
+* K tile   = [D/X][TT][X]             (X = 16 bytes / element size)
+* V tile   = [D/(16E)][TT/4][16][E][4] (E = X/4): each 16-byte group holds four
   consecutive tokens of E head-dim positions spaced 16 apart;
 * tiles are ordered block -> tile -> kv head (the Hkv heads' tiles of one tile
   slot of a block are adjacent).
@@ -56,8 +57,8 @@ class CacheLayout:
     dtype: str  # "f32" | "bf16"
 
     def __post_init__(self):
-        if self.block_size % TILE:
-            raise ValueError("block_size must be a multiple of 16")
+        if self.block_size != 8 and self.block_size % TILE:
+            raise ValueError("block_size must be 8 or a multiple of 16")
         if self.head_dim % (TILE * self.E):
             raise ValueError("head_dim must be a multiple of 16*E")
 
@@ -77,8 +78,13 @@ class CacheLayout:
         return self.X // 4
 
     @property
+    def tile_tokens(self) -> int:
+        """Tokens per tile: 16, or 8 for a block of 8."""
+        return min(self.block_size, TILE)
+
+    @property
     def tiles_per_block(self) -> int:
-        return self.block_size // TILE
+        return self.block_size // self.tile_tokens
 
     @property
     def cache_elems(self) -> int:
@@ -92,17 +98,17 @@ class CacheLayout:
 
     # -- views of the flat arrays ---------------------------------------------
     def _k6(self, k_cache):
-        """K as [block, head, tile, d//X, token%16, d%X] (stored tile-major)."""
-        N, H, T, D, X = (self.num_blocks, self.num_kv_heads, self.tiles_per_block,
-                         self.head_dim, self.X)
-        return k_cache.reshape(N, T, H, D // X, TILE, X).transpose(0, 2, 1, 3, 4, 5)
+        """K as [block, head, tile, d//X, token%TT, d%X] (stored tile-major)."""
+        N, H, T, D, X, TT = (self.num_blocks, self.num_kv_heads, self.tiles_per_block,
+                             self.head_dim, self.X, self.tile_tokens)
+        return k_cache.reshape(N, T, H, D // X, TT, X).transpose(0, 2, 1, 3, 4, 5)
 
     def _v8(self, v_cache):
-        """V as [block, head, tile, m, j, i, e, r]: token 4j+r, dim 16E*m + 16e + i
-        (stored tile-major)."""
-        N, H, T, D, E = (self.num_blocks, self.num_kv_heads, self.tiles_per_block,
-                         self.head_dim, self.E)
-        return v_cache.reshape(N, T, H, D // (TILE * E), 4, TILE, E, 4).transpose(
+        """V as [block, head, tile, m, j, i, e, r]: token 4j+r of the tile, dim
+        16E*m + 16e + i (stored tile-major)."""
+        N, H, T, D, E, TT = (self.num_blocks, self.num_kv_heads, self.tiles_per_block,
+                             self.head_dim, self.E, self.tile_tokens)
+        return v_cache.reshape(N, T, H, D // (TILE * E), TT // 4, TILE, E, 4).transpose(
             0, 2, 1, 3, 4, 5, 6, 7)
 
     # -- reads ----------------------------------------------------------------
@@ -125,7 +131,7 @@ class CacheLayout:
     def write_token(self, k_cache, v_cache, block, offset, k_tok, v_tok):
         """Store one token's [Hkv, D] key and value at (block, offset in block)."""
         H, D, X, E = self.num_kv_heads, self.head_dim, self.X, self.E
-        t, o = divmod(int(offset), TILE)
+        t, o = divmod(int(offset), self.tile_tokens)
         self._k6(k_cache)[block, :, t, :, o, :] = np.asarray(k_tok).reshape(H, D // X, X)
         j, r = divmod(o, 4)
         vt = np.asarray(v_tok).reshape(H, D // (TILE * E), E, TILE).transpose(0, 1, 3, 2)
