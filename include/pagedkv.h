@@ -49,30 +49,34 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
  * ([P1] section 2.2: fixed-size pages scattered through one pool; [P2]
  * PagedAttention > 工作原理 > 1. 页表管理: a per-sequence page table).
  *
- * Supported: block_size in {16, 32, 64}; head_dim in {64, 128};
- * dtype in {F32, BF16}.
+ * Supported: block_size in {8, 16, 32, 64} (8: every entry point but
+ * pa_paged_attn_prefill, which returns PA_ERR_UNSUPPORTED); head_dim in
+ * {64, 128}; dtype in {F32, BF16}.  Smaller blocks waste fewer slots at
+ * sequence ends but mean more table entries per token ([P1] section 3.4 on
+ * --block-size).
  *
  * Layout (the library's own choice; the pages fix only the logical picture).
  * Let s = element bytes, X = 16 / s (elements per 16-byte group), E = X / 4,
- * TPB = block_size / 16.  A block is cut into TPB tiles of 16 tokens; tiles
- * are ordered block -> tile -> kv head (the Hkv heads' tiles of one tile slot
- * are adjacent), each tile holding 16 * head_dim elements.  Element (block b,
- * head h, token slot o, dim d) sits at
+ * TT = min(block_size, 16) tokens per tile, TPB = block_size / TT.  A block is
+ * cut into TPB tiles of TT tokens; tiles are ordered block -> tile -> kv head
+ * (the Hkv heads' tiles of one tile slot are adjacent), each tile holding
+ * TT * head_dim elements.  Element (block b, head h, token slot o, dim d) sits at
  *
- *   K: ((((b*TPB + o/16)*Hkv + h)*(D/X) + d/X)*16 + o%16)*X + d%X
- *   V: ((b*TPB + o/16)*Hkv + h)*16*D
- *      + ((((d/(16E))*4 + (o%16)/4)*16 + d%16)*E + (d/16)%E)*4 + o%4
+ *   K: ((((b*TPB + o/TT)*Hkv + h)*(D/X) + d/X)*TT + o%TT)*X + d%X
+ *   V: ((b*TPB + o/TT)*Hkv + h)*TT*D
+ *      + ((((d/(16E))*(TT/4) + (o%TT)/4)*16 + d%16)*E + (d/16)%E)*4 + o%4
  *
  * so a K 16-byte group is X consecutive dims of one token, and a V 16-byte
  * group is 4 consecutive tokens of E dims spaced 16 apart.  One wavefront
- * reading a tile with one 16-byte load per lane per 1 KiB touches one
- * contiguous KiB per instruction.
+ * reading a 16-token tile with one 16-byte load per lane per 1 KiB touches one
+ * contiguous KiB per instruction (with blocks of 8, two runs of 512 bytes, one
+ * per block).
  *
  * A slot is b * block_size + o.  Bytes per array: pa_cache_bytes().
  */
 typedef struct pa_cache_desc {
     int32_t num_blocks;    /* N > 0                                   */
-    int32_t block_size;    /* B: 16, 32 or 64 tokens per block        */
+    int32_t block_size;    /* B: 8, 16, 32 or 64 tokens per block     */
     int32_t num_kv_heads;  /* Hkv > 0                                 */
     int32_t head_dim;      /* D: 64 or 128                            */
     int32_t dtype;         /* pa_dtype                                */

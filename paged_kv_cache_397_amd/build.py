@@ -28,6 +28,9 @@ OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.cpp", "allocator.cpp", "kernels_cache.hip", "kernels_decode.hip",
            "kernels_prefill.hip"]
+# decode_variant.hip is compiled once per decode kernel variant (load policy, decode
+# step, block size 8) so that the variants build in parallel.
+VARIANTS = [(stream, step, half) for stream in (0, 1) for step in (0, 1) for half in (0, 1)]
 PROBE_SOURCES = ["bandwidth_probe.hip"]
 ARCH = "gfx950"
 
@@ -67,12 +70,21 @@ def build(verbose: bool = False) -> str:
         objs[src] = obj
         lang = ["-x", "hip"] if src.endswith(".hip") or src == "api.cpp" else ["-x", "c++"]
         cmds.append([hipcc, *common, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+    variant_objs = []
+    for stream, step, half in VARIANTS:
+        obj = os.path.join(OBJ_DIR, f"decode_variant_{stream}{step}{half}.o")
+        variant_objs.append(obj)
+        cmds.append([hipcc, *common, "-x", "hip", f"-DPKV_STREAM={stream}", f"-DPKV_STEP={step}",
+                     f"-DPKV_HALF={half}", "-c", os.path.join(CSRC, "decode_variant.hip"), "-o", obj])
+    # the slowest (the decode variants) first
+    cmds.sort(key=lambda c: "decode_variant.hip" not in " ".join(c))
+    workers = max(1, min(len(cmds), os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    for lib, srcs in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+    for lib, objs_of in ((LIB, [objs[s] for s in SOURCES] + variant_objs),
+                         (PROBE_LIB, [objs[s] for s in PROBE_SOURCES])):
         tmp = lib + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[objs[s] for s in srcs],
-              "-o", tmp], verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs_of, "-o", tmp], verbose)
         os.replace(tmp, lib)
     return LIB
 

@@ -21,7 +21,8 @@ pa_status check_desc(const pa_cache_desc* d) {
     if (d->num_blocks <= 0 || d->block_size <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0)
         return PA_ERR_INVALID_ARG;
     if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16) return PA_ERR_INVALID_ARG;
-    if (d->block_size != 16 && d->block_size != 32 && d->block_size != 64) return PA_ERR_UNSUPPORTED;
+    if (d->block_size != 8 && d->block_size != 16 && d->block_size != 32 && d->block_size != 64)
+        return PA_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
@@ -331,7 +332,8 @@ pa_status decode_call(const pa_cache_desc* d, void* out, const void* q, const vo
     } else if (workspace_bytes < need) {
         return PA_ERR_INVALID_ARG;
     }
-    const int32_t tpb = d->block_size / pkv::kTile;
+    // tiles of the cache layout per block (a block of 8 tokens is one 8-token tile)
+    const int32_t tpb = d->block_size >= pkv::kTile ? d->block_size / pkv::kTile : 1;
     const int32_t rows = use_group ? d->num_kv_heads : num_q_heads;
     // Every tile position of the batch (rows x sequences x table columns) must fit in int32.
     const double positions = static_cast<double>(rows) * num_seqs * max_blocks_per_seq * tpb;
@@ -487,6 +489,8 @@ pa_status pa_paged_attn_prefill(const pa_cache_desc* d, void* out, const void* q
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
     const int32_t group = num_q_heads / d->num_kv_heads;
     if (d->dtype != PA_DTYPE_BF16 || 16 % group != 0) return PA_ERR_UNSUPPORTED;
+    // the prefill kernel stages 16-token tiles of one block each
+    if (d->block_size < pkv::kTile) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
     if (max_blocks_per_seq == 0) return PA_ERR_INVALID_ARG;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)

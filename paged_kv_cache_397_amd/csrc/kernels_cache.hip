@@ -44,7 +44,9 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     const int t0 = TW * static_cast<int>(blockIdx.x);
     const int h = blockIdx.y;
     const int lane = threadIdx.x;
-    const int tpb = block_size / kTile;
+    const int tt = block_size < kTile ? block_size : kTile;  // tokens per tile (8 or 16)
+    const int tshift = __builtin_ctz(static_cast<unsigned>(tt));
+    const int tpb = block_size / tt;
     const int bshift = __builtin_ctz(static_cast<unsigned>(block_size));  // a power of two
     // lane k < 16: token t0 + k's slot (-1 = skip), its tile's element offset and slot in tile
     long long my = -1;
@@ -57,8 +59,8 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     if (my >= 0) {
         const long long b = my >> bshift;
         const int o = static_cast<int>(my & (block_size - 1));
-        tb = ((b * tpb + (o >> 4)) * num_kv_heads + h) * static_cast<long long>(kTile * D);
-        ti = o & 15;
+        tb = ((b * tpb + (o >> tshift)) * num_kv_heads + h) * static_cast<long long>(tt * D);
+        ti = o & (tt - 1);
     }
     const long long n1 = __shfl_down(my, 1), n2 = __shfl_down(my, 2), n3 = __shfl_down(my, 3);
     const bool qstart = lane < TW - 3 && my >= 0 && (my & 3) == 0 && n1 == my + 1 &&
@@ -73,12 +75,13 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
         const int tir = __shfl(ti, r);
         if (!((valid >> r) & 1u)) continue;
         const size_t src = (static_cast<size_t>(t0 + r) * num_kv_heads + h) * D + c * X;
-        *reinterpret_cast<u32x4*>(k_cache + tbr + (c * 16 + tir) * X) =
+        *reinterpret_cast<u32x4*>(k_cache + tbr + (c * tt + tir) * X) =
             *reinterpret_cast<const u32x4*>(k + src);
         *reinterpret_cast<u32x4*>(&vrow[r][c * X]) = *reinterpret_cast<const u32x4*>(v + src);
     }
     __syncthreads();
     // V of each quad: group (m, j, i) holds dims 16E*m + 16e + i (e < E) of its 4 tokens
+    const int tq = tt >> 2;  // quads per tile
     for (uint32_t qm = qmask; qm != 0; qm &= qm - 1) {
         const int q = __builtin_ctz(qm);
         const long long tbq = readlane_i64(tb, q);
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) w[r] = static_cast<uint32_t>(vrow[q + r][16 * m + i]);
             }
-            *reinterpret_cast<u32x4*>(v_cache + tbq + (((m * 4 + j) * 16 + i) * E) * 4) = w;
+            *reinterpret_cast<u32x4*>(v_cache + tbq + (((m * tq + j) * 16 + i) * E) * 4) = w;
         }
     }
     // V of the tokens in no quad, element by element
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
         const int j = tir >> 2, rr = tir & 3;
         for (int d = lane; d < D; d += kWaveSize) {
             const int m = d / (16 * E), e = (d >> 4) % E, i = d & 15;
-            v_cache[tbr + ((((m * 4 + j) * 16 + i) * E + e) * 4 + rr)] = vrow[r][d];
+            v_cache[tbr + ((((m * tq + j) * 16 + i) * E + e) * 4 + rr)] = vrow[r][d];
         }
     }
 }
@@ -217,20 +220,21 @@ __global__ __launch_bounds__(D) void append_tokens_kernel(
     }
     for (int n = n0 + nwg * D; n < num_lens; n += nwg * D) lens_out[n] = lens_in[n];
     if (!tok) return;
-    const int tpb = block_size / kTile;
+    const int tt = block_size < kTile ? block_size : kTile;  // tokens per tile (8 or 16)
+    const int tpb = block_size / tt;
     if (slot < 0 || slot >= static_cast<int64_t>(num_blocks) * block_size) return;
     const int64_t b = slot / block_size;
     const int o = static_cast<int>(slot - b * block_size);
-    const int ti = o & 15;
+    const int ti = o % tt;
     const int j = ti >> 2, r = ti & 3;
     const int d = tid;
     const size_t tile_base =
-        ((static_cast<size_t>(b) * tpb + (o >> 4)) * num_kv_heads + h) * (kTile * D);
+        ((static_cast<size_t>(b) * tpb + o / tt) * num_kv_heads + h) * (static_cast<size_t>(tt) * D);
     const size_t src = (static_cast<size_t>(t) * num_kv_heads + h) * D;
     const int m = d / (16 * E), ee = (d >> 4) % E, i = d & 15;
-    v_cache[tile_base + ((((m * 4 + j) * 16 + i) * E + ee) * 4 + r)] = v[src + d];
+    v_cache[tile_base + ((((m * (tt / 4) + j) * 16 + i) * E + ee) * 4 + r)] = v[src + d];
     if (d % X == 0)
-        *reinterpret_cast<u32x4*>(k_cache + tile_base + ((d / X) * 16 + ti) * X) =
+        *reinterpret_cast<u32x4*>(k_cache + tile_base + ((d / X) * tt + ti) * X) =
             *reinterpret_cast<const u32x4*>(k + src + d);
 }
 

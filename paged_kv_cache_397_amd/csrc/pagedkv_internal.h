@@ -7,7 +7,8 @@
 
 namespace pkv {
 
-constexpr int kTile = 16;  // tokens per tile (a block holds block_size / 16 tiles)
+constexpr int kTile = 16;  // tokens per tile (a block holds block_size / 16 tiles; a block of 8
+                           // tokens is one 8-token tile, and decode reads two per tile)
 constexpr int kWave = 64;  // CDNA wavefront width
 
 // Everything pass 1 and pass 2 of decode need; passed by value to both kernels.
@@ -122,5 +123,10 @@ hipError_t launch_decode(int dtype, int head_dim, bool use_group_kernel, const D
 // DecodeArgs' step fields set).
 hipError_t launch_decode_step(int dtype, int head_dim, bool use_group_kernel, const DecodeArgs& a,
                               hipStream_t stream);
+// The decode kernels of one variant: Stream = non-temporal K/V loads, Step = the
+// decode step, Half = blocks of 8 tokens (instantiated in decode_variant.hip).
+template <bool Stream, bool Step, bool Half>
+hipError_t launch_decode_variant(int dtype, int head_dim, bool use_group_kernel, const DecodeArgs& a,
+                                 int passes, hipStream_t stream);
 
 }  // namespace pkv

@@ -45,7 +45,8 @@ def test_cache_bytes_and_descriptor_checks():
     lib = N.lib()
     assert lib.pa_cache_bytes(ctypes.byref(_desc())) == 16 * 2 * 16 * 64 * 2
     assert lib.pa_cache_bytes(ctypes.byref(_desc(dtype=0))) == 16 * 2 * 16 * 64 * 4
-    for bad in (dict(block_size=8), dict(head_dim=96), dict(num_blocks=0), dict(dtype=7)):
+    for bad in (dict(block_size=12), dict(block_size=128), dict(head_dim=96), dict(num_blocks=0),
+                dict(dtype=7)):
         assert lib.pa_cache_bytes(ctypes.byref(_desc(**bad))) == 0
 
 
@@ -135,6 +136,7 @@ def test_prefill_argument_checks_without_a_gpu():
     assert lib.pa_paged_attn_prefill(*args(f32, 4)) == S            # no fp32 prefill kernel
     assert lib.pa_paged_attn_prefill(*args(bf16, 6)) == S           # G = 3 does not divide 16
     assert lib.pa_paged_attn_prefill(*args(bf16, 64)) == S          # G = 32
+    assert lib.pa_paged_attn_prefill(*args(N.CacheDesc(64, 8, 2, 64, 1), 4)) == S  # blocks of 8
     assert lib.pa_paged_attn_prefill(*args(bf16, 5)) == N.PA_ERR_INVALID_ARG  # Hq % Hkv != 0
     assert lib.pa_paged_attn_prefill(*args(bf16, 4, T=-1)) == N.PA_ERR_INVALID_ARG
     assert lib.pa_paged_attn_prefill(*args(bf16, 4, mql=-1)) == N.PA_ERR_INVALID_ARG

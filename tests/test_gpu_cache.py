@@ -24,7 +24,8 @@ def _random_pool(spec, seed):
 
 
 @pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 16), ("bf16", 64, 32), ("f32", 64, 16),
-                                       ("f32", 128, 64), ("bf16", 128, 64)])
+                                       ("f32", 128, 64), ("bf16", 128, 64), ("bf16", 128, 8),
+                                       ("f32", 64, 8)])
 def test_reshape_and_cache_bitexact(dtype, D, B):
     spec = ops.CacheSpec(num_blocks=12, block_size=B, num_kv_heads=3, head_dim=D, dtype=dtype)
     lay = CacheLayout(12, 3, B, D, dtype)
@@ -57,7 +58,7 @@ def _prompt_runs(rng, num_slots, lengths):
 
 
 @pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 16), ("bf16", 64, 32), ("f32", 128, 16),
-                                       ("f32", 64, 64)])
+                                       ("f32", 64, 64), ("bf16", 64, 8)])
 def test_reshape_and_cache_prompt_runs_bitexact(dtype, D, B):
     """Chunks of consecutive slots whose lengths and starts are not multiples of 4, so
     the kernel's four-slot groups begin at every offset of its 16-token windows, mixed
@@ -126,7 +127,7 @@ def test_reshape_and_cache_skips_out_of_range_slots():
     assert np.array_equal(to_storage(kd), kc) and np.array_equal(to_storage(vd), vc)
 
 
-@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f32", 32)])
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f32", 32), ("bf16", 8)])
 def test_copy_blocks_bitexact(dtype, B):
     spec = ops.CacheSpec(num_blocks=10, block_size=B, num_kv_heads=4, head_dim=128, dtype=dtype)
     lay = CacheLayout(10, 4, B, 128, dtype)
@@ -164,7 +165,8 @@ def _oracle_step(lay, kc, vc, tables, k, v, slots, cows, updates):
     oracle_reshape_and_cache(lay, k, v, slots, kc, vc)
 
 
-@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 16), ("f32", 64, 32), ("bf16", 64, 16)])
+@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 16), ("f32", 64, 32), ("bf16", 64, 16),
+                                       ("bf16", 128, 8)])
 def test_append_tokens_with_copy_on_write_bitexact(dtype, D, B):
     """Forked sequences that share a partial block append one token each in one step:
     all but the last sharer copy the block first; the table updates and the token
@@ -208,7 +210,8 @@ def test_append_tokens_with_copy_on_write_bitexact(dtype, D, B):
     assert np.array_equal(tables, expect)          # the updates rebuild the allocator's tables
 
 
-@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 16), ("f32", 64, 32), ("bf16", 128, 64)])
+@pytest.mark.parametrize("dtype,D,B", [("bf16", 128, 16), ("f32", 64, 32), ("bf16", 128, 64),
+                                       ("bf16", 128, 8)])
 @pytest.mark.parametrize("pinned", [False, True])
 def test_append_tokens_several_tokens_of_forked_sequences_bitexact(dtype, D, B, pinned):
     """One call appends several tokens to each of four sequences forked from one

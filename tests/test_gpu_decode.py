@@ -64,6 +64,9 @@ EDGE_CTX = [0, 1, 15, 16, 17, 33, 100, 257]
     ("bf16", 64, 16, 16, 1),   # group, G = 16
     ("f32", 64, 16, 2, 2),     # fp32 per-head
     ("f32", 128, 32, 6, 2),    # fp32 with G = 3 (per-head path)
+    ("bf16", 128, 8, 32, 8),   # blocks of 8 tokens: a tile reads two blocks; group, G = 4
+    ("bf16", 128, 8, 8, 8),    # blocks of 8, per-head path
+    ("f32", 64, 8, 4, 2),      # blocks of 8, fp32
 ])
 @pytest.mark.parametrize("units", [0, 1, 3, 40])
 def test_decode_matches_oracle(dtype, D, B, Hq, Hkv, units):
@@ -145,13 +148,31 @@ def test_context_lengths_outside_the_table_are_clamped(dtype, Hq, Hkv, units):
     assert not to_float64(got[3], dtype).any()
 
 
-@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 32, 8), ("bf16", 8, 8)])
-def test_unit_count_sweep(dtype, Hq, Hkv):
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 16, 4), ("bf16", 8, 8), ("f32", 4, 2)])
+@pytest.mark.parametrize("units", [0, 3, 40])
+def test_blocks_of_8_with_an_odd_table_width(dtype, Hq, Hkv, units):
+    """Blocks of 8 tokens and five table columns (a row addresses 40 tokens), so the
+    last 16-token tile of a full row has one block only: lengths past 40 act as 40,
+    equal bit for bit to the call with the clamped lengths and to the oracle, with
+    the pool's unused blocks NaN-poisoned."""
+    true_ctx = [40, 8, 33, 0, 5, 39, 16, 17]
+    spec = ops.CacheSpec(num_blocks=64, block_size=8, num_kv_heads=Hkv, head_dim=128, dtype=dtype)
+    b = Batch(spec, true_ctx, Hq, seed=34, free_order=gen.pool_permutation(9, 64), max_blocks=5)
+    wild = torch.tensor([41, 8, 33, -1, 5, 39, 16, 17], dtype=torch.int32, device="cuda")
+    got = b.run(num_units=units, ctx=wild)
+    assert np.array_equal(got.view(np.uint8), b.run(num_units=units).view(np.uint8))
+    assert not np.isnan(to_float64(got, dtype)).any()
+    assert_close(to_float64(got, dtype), b.expected(), dtype, f"blocks of 8, units {units}")
+    assert not to_float64(got[3], dtype).any()
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,B", [("bf16", 32, 8, 16), ("bf16", 8, 8, 16), ("bf16", 32, 8, 8)])
+def test_unit_count_sweep(dtype, Hq, Hkv, B):
     """Every split of the work (one unit .. more units than tiles) stays within tolerance."""
     rng = gen.stream(41, 1)
     ctx = rng.integers(1, 700, 12)
-    spec = ops.CacheSpec(num_blocks=1024, block_size=16, num_kv_heads=Hkv, head_dim=128, dtype=dtype)
-    b = Batch(spec, ctx, Hq, seed=41, free_order=gen.pool_permutation(4, 1024))
+    spec = ops.CacheSpec(num_blocks=2048, block_size=B, num_kv_heads=Hkv, head_dim=128, dtype=dtype)
+    b = Batch(spec, ctx, Hq, seed=41, free_order=gen.pool_permutation(4, 2048))
     ref = b.expected()
     for units in (1, 2, 7, 64, 513, 5000, 0):
         assert_close(to_float64(b.run(num_units=units), dtype), ref, dtype, f"units {units}")

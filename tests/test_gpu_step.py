@@ -135,6 +135,9 @@ def _run(dtype, D, B, Hq, Hkv, units, seed, steps=3, forked=True, skip_some=True
     ("bf16", 128, 64, 16, 2),    # group, G = 8, four tiles per block
     ("f32", 64, 16, 4, 2),       # fp32 per-head path, two rows per KV head
     ("f32", 128, 32, 2, 2),
+    ("bf16", 128, 8, 32, 8),     # blocks of 8 tokens: a tile reads two blocks
+    ("bf16", 128, 8, 8, 8),      # blocks of 8, per-head path
+    ("f32", 64, 8, 4, 2),        # blocks of 8, fp32
 ])
 @pytest.mark.parametrize("units", [0, 7, 40])
 def test_step_equals_append_then_decode(dtype, D, B, Hq, Hkv, units):
