@@ -124,20 +124,23 @@ __device__ __forceinline__ void pair_scores(f32x4 (&S0)[NB], f32x4 (&S1)[NB],
     }
 }
 
-// Folding one pair's scores into the wave's NB query blocks, in two steps so that
-// the next pair's score products can run between them: fold_max takes the scores to
-// base 2 units with masks, updates each column's reference maximum and rescales
-// the accumulators when it moves; fold_pv forms the weights and accumulates
-// O^T += V^T P^T and l += 1 P^T.  kEdge: some key of the pair may be past a column's
-// causal limit or past the sequence end: per-column masks, and V rows at or past
-// vlim zeroed (they may hold anything, and a zero weight times NaN is NaN).
-// Otherwise every key is visible to every column.  c >= 0 (scale * log2 e).
+// Folding one pair's scores into the wave's NB query blocks, in pieces that run on
+// different units so that one pair's vector work can overlap another pair's matrix
+// work:
+//   pair_max (VALU): scores to base-2 units with masks, each column's maximum, and
+//     whether any column's reference maximum has to move;
+//   rescale (VALU, rare): move the reference maxima, rescale the accumulators;
+//   pair_weights (VALU): the weights exp2(score - m), rounded to bf16;
+//   pair_pv (MFMA): O^T += V^T P^T and l += 1 P^T.
+// kEdge: some key of the pair may be past a column's causal limit or past the
+// sequence end: per-column masks, and V rows at or past vlim zeroed (they may hold
+// anything, and a zero weight times NaN is NaN).  Otherwise every key is visible to
+// every column.  c >= 0 (scale * log2 e).
 template <int D, int NB, bool kEdge>
-__device__ __forceinline__ void fold_max(ColState<D> (&st)[NB], float (&x)[NB][8],
-                                         const f32x4 (&S0)[NB], const f32x4 (&S1)[NB], int key0,
-                                         const int (&lim)[NB], float c, int j) {
-    constexpr int NG = D / 16;
-    float mx[NB];
+__device__ __forceinline__ bool pair_max(const ColState<D> (&st)[NB], float (&x)[NB][8],
+                                         float (&mx)[NB], const f32x4 (&S0)[NB],
+                                         const f32x4 (&S1)[NB], int key0, const int (&lim)[NB],
+                                         float c, int j) {
     bool any = false;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -158,24 +161,26 @@ __device__ __forceinline__ void fold_max(ColState<D> (&st)[NB], float (&x)[NB][8
         mx[b] = column_max(m8) * c;
         any |= mx[b] > st[b].m + kMaxSlack;
     }
-    if (__ballot(any)) {
+    return any;
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void rescale(ColState<D> (&st)[NB], const float (&mx)[NB]) {
+    constexpr int NG = D / 16;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const float mn = mx[b] > st[b].m + kMaxSlack ? mx[b] : st[b].m;
-            const float alpha = fast_exp2(st[b].m - mn);
+    for (int b = 0; b < NB; ++b) {
+        const float mn = mx[b] > st[b].m + kMaxSlack ? mx[b] : st[b].m;
+        const float alpha = fast_exp2(st[b].m - mn);
 #pragma unroll
-            for (int g = 0; g < NG; ++g) st[b].acc[g] *= alpha;
-            st[b].lsum *= alpha;
-            st[b].m = mn;
-        }
+        for (int g = 0; g < NG; ++g) st[b].acc[g] *= alpha;
+        st[b].lsum *= alpha;
+        st[b].m = mn;
     }
 }
 
-template <int D, int NB, bool kEdge>
-__device__ __forceinline__ void fold_pv(ColState<D> (&st)[NB], const float (&x)[NB][8],
-                                        u32x4 (&va)[D / 16], int key0, int vlim, float c, int j) {
-    constexpr int NG = D / 16;
-    bf16x8 pB[NB];
+template <int D, int NB>
+__device__ __forceinline__ void pair_weights(bf16x8 (&pB)[NB], const ColState<D> (&st)[NB],
+                                             const float (&x)[NB][8], float c) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         uint32_t pw[4];
@@ -185,6 +190,12 @@ __device__ __forceinline__ void fold_pv(ColState<D> (&st)[NB], const float (&x)[
                               fast_exp2(__builtin_fmaf(x[b][2 * r + 1], c, -st[b].m)));
         pB[b] = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
     }
+}
+
+template <int D, int NB, bool kEdge>
+__device__ __forceinline__ void pair_pv(ColState<D> (&st)[NB], const bf16x8 (&pB)[NB],
+                                        u32x4 (&va)[D / 16], int key0, int vlim, int j) {
+    constexpr int NG = D / 16;
     // the V operands were read by inline asm the compiler does not track: wait here
 #pragma unroll
     for (int g = 0; g < NG; ++g) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(va[g]));
@@ -212,6 +223,19 @@ __device__ __forceinline__ void fold_pv(ColState<D> (&st)[NB], const float (&x)[
     for (int b = 0; b < NB; ++b)
         st[b].lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(one2, one2, one2, one2),
                                                              pB[b], st[b].lsum, 0, 0, 0);
+}
+
+// Scheduling hints: within the current region, alternate n_mfma groups of one matrix
+// instruction with `valu` vector instructions each, so that one pair's softmax runs
+// on the vector ALUs while the matrix cores work on another pair (the compiler would
+// otherwise cluster each kind).
+template <int NMfma, int Valu>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+    for (int k = 0; k < NMfma; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, Valu, 0);  // then VALU instructions
+    }
 }
 
 template <int D, int G>
@@ -425,10 +449,16 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // Software pipeline: the loop step for pair p computes the scores of pair p + 1
-    // (matrix cores) while it folds pair p (softmax on the vector ALUs, then PV).
-    // Pair 0's scores first: wait for its copies (later pairs' may stay in flight).
+    // Software pipeline.  Step p folds pair p and prepares pair p + 1 in two phases,
+    // each pairing one unit's work on one pair with the other unit's on the other:
+    //   A: the weights of pair p (vector ALUs)  |  the scores of pair p + 1 (matrix)
+    //   B: O += V P of pair p (matrix)          |  the maxima of pair p + 1 (vector)
+    // then, rarely, pair p + 1's rescale.  Pair 0's scores and maxima come first:
+    // wait for its copies (later pairs' may stay in flight).
+    // Pairs below p_fast are unmasked; the last pair is always masked (pf <= np - 1).
+    const int pf = min(p_fast, np - 1);
     f32x4 S0[kQB], S1[kQB];
+    float x[kQB][8];
     if (np >= kStages - 1)
         __builtin_amdgcn_s_waitcnt(0x0F70 | ((kStages - 2) * LPT));
     else
@@ -440,13 +470,19 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int k = 0; k < NL; ++k) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k0[k]), "+v"(k1[k]));
         pair_scores<D, kQB>(S0, S1, q, k0, k1);
+        float mx[kQB];
+        const bool any = pf == 0 ? pair_max<D, kQB, true>(st, x, mx, S0, S1, 0, lim, cs, j)
+                                 : pair_max<D, kQB, false>(st, x, mx, S0, S1, 0, lim, cs, j);
+        if (__ballot(any)) rescale<D, kQB>(st, mx);
     }
 
     // Step p: wait for pair p + 1's copies and barrier (pair p - 1's buffer is then
-    // free: its K was read in step p - 2, its V in step p - 1), start the copy of pair
-    // p + 3 into it, read K of pair p + 1 and V of pair p, score pair p + 1, fold pair p.
-    auto pair_step = [&](int p, auto edge, auto next) {
+    // free: its K was read in step p - 1, its V in step p - 1), start the copy of pair
+    // p + 3 into it, read K of pair p + 1 and V of pair p, then phases A and B.
+    // kEdge: pair p is masked; kEdgeNext: pair p + 1 is.
+    auto pair_step = [&](int p, auto edge, auto edge_next, auto next) {
         constexpr bool kEdge = decltype(edge)::value;
+        constexpr bool kEdgeNext = decltype(edge_next)::value;
         constexpr bool kNext = decltype(next)::value;
         if constexpr (kNext) {
             if (p + kStages - 1 <= np)
@@ -460,11 +496,11 @@ void prefill_kernel(PrefillArgs a) {
         f32x4 N0[kQB], N1[kQB];
         if constexpr (kNext) read_k(p + 1, k0, k1);
         read_v(p, va);
-        // Near the diagonal or the sequence end every block is masked; a block that
+        // A.  Near the diagonal or the sequence end every block is masked; a block that
         // sees no key of the pair adds exact zeros (its maximum is already finite:
         // every column sees key 0 in pair 0).
-        float x[kQB][8];
-        fold_max<D, kQB, kEdge>(st, x, S0, S1, p * kPairKeys, lim, cs, j);
+        bf16x8 pB[kQB];
+        pair_weights<D, kQB>(pB, st, x, cs);
         if constexpr (kNext) {
             // 2 NG V reads were issued after the K reads: at most min(2 NG, 15) LDS reads
             // outstanding leaves every K read done
@@ -472,22 +508,26 @@ void prefill_kernel(PrefillArgs a) {
             for (int k = 0; k < NL; ++k)
                 asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(k0[k]), "+v"(k1[k]) : "i"(2 * NG > 15 ? 15 : 2 * NG));
             pair_scores<D, kQB>(N0, N1, q, k0, k1);
+            interleave_mfma_valu<4 * NL * kQB, 3>();
         }
-        fold_pv<D, kQB, kEdge>(st, x, va, p * kPairKeys, L, cs, j);
+        // B
+        pair_pv<D, kQB, kEdge>(st, pB, va, p * kPairKeys, L, j);
         if constexpr (kNext) {
-#pragma unroll
-            for (int b = 0; b < kQB; ++b) {
-                S0[b] = N0[b];
-                S1[b] = N1[b];
-            }
+            float mx[kQB];
+            const bool any = pair_max<D, kQB, kEdgeNext>(st, x, mx, N0, N1, (p + 1) * kPairKeys,
+                                                         lim, cs, j);
+            interleave_mfma_valu<(NG + 1) * kQB, 2>();
+            if (__ballot(any)) rescale<D, kQB>(st, mx);
         }
     };
-    // Pairs below p_fast are unmasked; the last pair is always masked (pf <= np - 1).
-    const int pf = min(p_fast, np - 1);
     int p = 0;
-    for (; p < pf; ++p) pair_step(p, std::false_type{}, std::true_type{});
-    for (; p < np - 1; ++p) pair_step(p, std::true_type{}, std::true_type{});
-    pair_step(np - 1, std::true_type{}, std::false_type{});
+    for (; p + 1 < pf; ++p) pair_step(p, std::false_type{}, std::false_type{}, std::true_type{});
+    if (p < pf) {
+        pair_step(p, std::false_type{}, std::true_type{}, std::true_type{});
+        ++p;
+    }
+    for (; p < np - 1; ++p) pair_step(p, std::true_type{}, std::true_type{}, std::true_type{});
+    pair_step(np - 1, std::true_type{}, std::true_type{}, std::false_type{});
 
 #pragma unroll
     for (int b = 0; b < kQB; ++b) {
