@@ -175,6 +175,116 @@ def cpu_baseline(cfg, ctx, q_host, seconds):
             "single_thread": single}
 
 
+def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, units, ws, order,
+                      gtok):
+    """The trace as a serving loop: each step the host plans it with a fresh library
+    scheduler, writes its metadata into a pinned ring slot, uploads the slot with
+    one copy and launches the step's kernels; the device runs behind the host, so
+    the host's planning of step n + 1 overlaps the device's step n.  Returns the
+    device timeline per step (events at step `lo` and after the last step: host
+    bubbles included) and the host's own time per step."""
+    import torch
+    from paged_kv_cache_397_amd import ops
+    from paged_kv_cache_397_amd.scheduler import TraceScheduler
+
+    B, D, Hq, Hkv = spec.block_size, spec.head_dim, cfg.num_q_heads, cfg.num_kv_heads
+    sched = TraceScheduler(cfg.num_blocks, B, cfg.chunk, order, gen_tokens=gtok)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed + 1)
+    dt = spec.torch_dtype
+    pool = {"pk": (pmax, Hkv), "pv": (pmax, Hkv), "pq": (pmax, Hq), "k": (smax, Hkv),
+            "v": (smax, Hkv), "q": (smax, Hq)}
+    pool = {k: torch.randn(n, h, D, generator=g, device="cuda", dtype=dt) for k, (n, h) in pool.items()}
+    pout = torch.empty(pmax, Hq, D, device="cuda", dtype=dt)
+    dout = torch.empty(smax, Hq, D, device="cuda", dtype=dt)
+    # one slot's layout: (name, dtype, count), each field 256-byte aligned
+    fields = [("pslots", np.int64, pmax), ("pqs", np.int32, cmax + 1), ("pctx", np.int32, cmax),
+              ("ptables", np.int32, cmax * max_blocks), ("dslots", np.int64, smax),
+              ("cows", np.int32, 2 * smax), ("tables", np.int32, smax * max_blocks),
+              ("ctx", np.int32, smax)]
+    offs, o = {}, 0
+    for name, dtp, cnt in fields:
+        offs[name] = (o, dtp, cnt)
+        o += -(-cnt * np.dtype(dtp).itemsize // 256) * 256
+    slot_bytes = o
+    ring = 4
+    pinned = [torch.empty(slot_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(ring)]
+    host_views = [{n: p.numpy()[a:a + c * np.dtype(t).itemsize].view(t) for n, (a, t, c) in offs.items()}
+                  for p in pinned]
+    dev = torch.empty(slot_bytes, dtype=torch.uint8, device="cuda")
+    tdt = {np.int64: torch.int64, np.int32: torch.int32}
+    dev_views = {n: dev[a:a + c * np.dtype(t).itemsize].view(tdt[t]) for n, (a, t, c) in offs.items()}
+    ring_ev = [None] * ring
+    stream = torch.cuda.current_stream()
+    lo = min(50, cfg.steps - 1)
+    ev_lo, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    host_s, wait_s = [], []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for n in range(cfg.steps):
+        h0 = time.perf_counter()
+        if n == lo:
+            ev_lo.record(stream)
+        plan = sched.step(n, packed[n])
+        k = n % ring
+        w0 = time.perf_counter()
+        if ring_ev[k] is not None:
+            ring_ev[k].synchronize()  # the slot's previous upload has been read
+        wait_s.append(time.perf_counter() - w0)
+        hv = host_views[k]
+        P, C, S = plan.prefill_tokens(), len(plan.prefill_rids), len(plan.decode_rids)
+        if P:
+            hv["pslots"][:P] = plan.prefill_slots
+            hv["pqs"][0] = 0
+            np.cumsum(plan.prefill_count, out=hv["pqs"][1:C + 1])
+            hv["pctx"][:C] = plan.prefill_start + plan.prefill_count
+            sched.alloc.batch_metadata(plan.prefill_rids, max_blocks,
+                                       tables=hv["ptables"][:C * max_blocks].reshape(C, max_blocks),
+                                       ctx=np.empty(C, dtype=np.int32))
+        if S:
+            hv["dslots"][:S] = plan.decode_slots
+            hv["cows"][:2 * S] = plan.decode_cows.reshape(-1)
+            sched.alloc.batch_metadata(plan.decode_rids, max_blocks,
+                                       tables=hv["tables"][:S * max_blocks].reshape(S, max_blocks),
+                                       ctx=hv["ctx"][:S])
+        dev.copy_(pinned[k], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        ring_ev[k] = ev
+        if P:
+            ops.reshape_and_cache(spec, pool["pk"][:P], pool["pv"][:P], dev_views["pslots"][:P], kc, vc)
+            ops.paged_attn_prefill(spec, pout[:P], pool["pq"][:P], kc, vc,
+                                   dev_views["ptables"][:C * max_blocks].view(C, max_blocks),
+                                   dev_views["pqs"][:C + 1], dev_views["pctx"][:C], cfg.scale,
+                                   max_query_len=int(plan.prefill_count.max()))
+        if S:
+            ops.append_tokens(spec, pool["k"][:S], pool["v"][:S], dev_views["dslots"][:S], kc, vc,
+                              cow_pairs=(dev_views["cows"][:2 * S].view(S, 2)
+                                         if plan.num_decode_cows else None))
+            ops.paged_attn_decode(spec, dout[:S], pool["q"][:S], kc, vc,
+                                  dev_views["tables"][:S * max_blocks].view(S, max_blocks),
+                                  dev_views["ctx"][:S], cfg.scale, units, ws,
+                                  keep_cached=bool(cfg.prefix))
+        host_s.append(time.perf_counter() - h0)
+    ev_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = ev_lo.elapsed_time(ev_end) * 1e3 / (cfg.steps - lo)
+    ws_ = np.array(wait_s[lo:]) * 1e6
+    hs = np.array(host_s[lo:]) * 1e6 - ws_
+    return {"note": "a fresh scheduler plans each step while the device runs the previous ones; "
+                    "one pinned-to-device copy of the step's metadata per step; device timeline "
+                    "from step %d to the end over the steps, host bubbles included" % lo,
+            "us_per_step": round(float(per), 2),
+            "host_us_per_step": {"mean": round(float(hs.mean()), 2),
+                                 "p99": round(float(np.percentile(hs, 99)), 2),
+                                 "note": "planning, metadata and launches; the wait for a free "
+                                         "ring slot (the host is ahead of the device) excluded"},
+            "ring_wait_us_per_step_mean": round(float(ws_.mean()), 2),
+            "wall_ms_all_steps": round(wall * 1e3, 2),
+            "metadata_bytes_per_upload": int(slot_bytes)}
+
+
 def run_trace(args):
     """The continuous-batching trace: the library scheduler plans every step on the
     host (timed separately), then each step's device work runs on inputs already in
@@ -195,16 +305,21 @@ def run_trace(args):
     if cfg.prefix:
         max_blocks = -(-(cfg.open_hi + cfg.suffix_hi + cfg.out_hi) // B)
     order = gen.pool_permutation(cfg.seed, cfg.num_blocks)
-    sched = TraceScheduler(cfg.num_blocks, B, cfg.chunk, order,
-                           gen_token=cfg.gen_token if cfg.prefix else None)
+    gtok = cfg.gen_tokens if cfg.prefix else None
+    sched = TraceScheduler(cfg.num_blocks, B, cfg.chunk, order, gen_tokens=gtok)
     arrivals = [cfg.arrivals(n) for n in range(cfg.steps)]
+    # The arrivals packed as the scheduler takes them (prompts' and replayed outputs'
+    # token IDs included), outside every timed region: they are the trace's input.
+    packed, rid = [], 0
+    for a in arrivals:
+        packed.append(sched.pack(a, rid))
+        rid += len(packed[-1])
     plans, host_s = [], []
     for n in range(cfg.steps):
         t0 = time.perf_counter()
-        plan = sched.step(n, arrivals[n])
+        plan = sched.step(n, packed[n])
         tables, ctx = sched.alloc.batch_metadata(plan.decode_rids, max_blocks)
-        prids = np.array([r for r, _, _, _ in plan.prefill], dtype=np.int64)
-        ptables, _ = sched.alloc.batch_metadata(prids, max_blocks)
+        ptables, _ = sched.alloc.batch_metadata(plan.prefill_rids, max_blocks)
         host_s.append(time.perf_counter() - t0)
         plans.append((plan, tables, ctx, ptables))
     log(f"scheduled {cfg.steps} steps on the host")
@@ -290,6 +405,15 @@ def run_trace(args):
     t_step = np.array([a.elapsed_time(c) for a, _, c in evs]) * 1e-3
     t_attn = np.array([b.elapsed_time(c) for _, b, c in evs]) * 1e-3
     t_pre = np.array([a.elapsed_time(b) for a, b in evp]) * 1e-3
+    pmax_all = max([d["P"] for d in steps_dev] + [1])
+    smax_all = max([d["S"] for d in steps_dev] + [1])
+    cmax_all = max([len(pl.prefill) for pl, _, _, _ in plans] + [1])
+    for d in steps_dev:  # the per-step inputs; the end-to-end loop below draws from pools
+        for k in [k for k, v in d.items() if isinstance(v, torch.Tensor)]:
+            del d[k]
+    torch.cuda.empty_cache()
+    e2e = _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax_all, smax_all, cmax_all,
+                            units, ws, order, gtok)
     pflops = np.array([d.get("pflops", 0.0) for d in steps_dev])
     kv_tok = 2 * Hkv * D * spec_elem_bytes(cfg.dtype)
     kv_bytes = np.array([d["ctx_sum"] for d in steps_dev], dtype=np.float64) * kv_tok
@@ -334,6 +458,7 @@ def run_trace(args):
                              "library_us_per_step_mean_same_steps":
                                  round(float(np.mean(host_s[:model_steps])) * 1e6, 2)},
         "wall_ms_all_steps": round(wall * 1e3, 2),
+        "end_to_end": e2e,
     }
     print(json.dumps(result), flush=True)
 
@@ -610,14 +735,17 @@ def run_blocksize(args):
         pg, ct, fx = [], [], []
         for n in range(tr.steps):
             sch.step(n, arrivals[n])
-            if n < 50 or not sch.running:
+            if n < 50:
+                continue
+            rids, prompts, lens = sch.running_info()
+            if not len(rids):
                 continue
             # tokens held over slots reserved: the allocator's own block count (paged),
             # prompt + the largest allowed output, and a fixed 4096 per request
-            held = sum(r.length for r in sch.running)
+            held = int(lens.sum())
             pg.append(held / ((N - sch.alloc.num_free()) * B))
-            ct.append(held / sum(r.prompt + tr.out_hi for r in sch.running))
-            fx.append(held / (4096 * len(sch.running)))
+            ct.append(held / int((prompts.astype(np.int64) + tr.out_hi).sum()))
+            fx.append(held / (4096 * len(rids)))
         util[B] = {"paged_mean": round(float(np.mean(pg)), 4), "paged_min": round(float(np.min(pg)), 4),
                    "contiguous_mean": round(float(np.mean(ct)), 4),
                    "fixed_4096_mean": round(float(np.mean(fx)), 4)}

@@ -508,6 +508,96 @@ pa_status pa_alloc_prefix_stats(const pa_allocator* a, int64_t* lookups, int64_t
 /* 1 and *key when the block is cached, 0 when not, -1 if out of range. */
 int32_t   pa_alloc_block_cached(const pa_allocator* a, int32_t block, uint64_t* key);
 
+/*
+ * Continuous-batching scheduler: the host side of a serving loop over its own
+ * allocator ([P2] vLLM 的调度 > 调度流程 and Preemption（抢占）; [P1] section 2.3).
+ * Each pa_sched_step, in this order:
+ *   1. requests that have produced their whole output release their blocks;
+ *   2. the requests added since the last step join the waiting queue's tail;
+ *   3. swapped-out requests come back first, in swap-out order, while their blocks fit;
+ *   4. waiting requests are admitted first come, first served while the whole
+ *      prompt fits (the first that does not fit blocks the queue; none is admitted
+ *      while a swapped request waits); with prefix caching, admission reuses the
+ *      cached full blocks of the prompt's opening and prefill starts after them;
+ *   5. every request whose prompt was complete before this step appends one
+ *      decode token, in running order; when no block is free the running request
+ *      admitted last is preempted (it may be the requester): swapped out when the
+ *      host pool holds its blocks, else freed and queued at the waiting queue's
+ *      head to recompute its prompt plus the tokens it has generated;
+ *   6. every running request whose prompt is not fully written gets its next chunk
+ *      of at most `chunk` prompt tokens, in running order (after the appends, so a
+ *      request preempted in this step holds no chunk of it); with prefix caching
+ *      each chunk's full blocks are then offered to the cache;
+ *   7. with prefix caching, each decode token that completes a block offers it.
+ * The plan says what the caller writes and attends: prompt chunks (slots), decode
+ * tokens (slots, copy-on-write pairs) and swap copies.  The caller runs a step's
+ * device work as: swap-in copies, prompt writes and prefill, swap-out copies,
+ * decode writes and decode.
+ *
+ *   pa_sched_create    num_host_blocks > 0 enables swap preemption; prefix_caching
+ *                      != 0 makes requests carry token IDs.
+ *   pa_sched_allocator the scheduler's allocator (owned by it; valid until destroy),
+ *                      for block tables and statistics; do not add or free through it.
+ *   pa_sched_add_requests  n requests (ids returned in rids, consecutive from 0 in
+ *                      creation order); they join the queue at the next step.
+ *                      prompt_tokens: the prompts concatenated (prefix caching only,
+ *                      else NULL); out_tokens: NULL or the out_lens[k] tokens each
+ *                      request generates, concatenated (prefix caching: the ID of the
+ *                      token appended at position prompt_len + g; a replayed trace
+ *                      knows them, a live loop passes them with pa_sched_push_tokens
+ *                      as it samples them).
+ *   pa_sched_push_tokens  append a token ID to each named request's known outputs.
+ *   pa_sched_step      run one step; *plan points into the scheduler's own arrays,
+ *                      valid until the next step or destroy.  PA_ERR_STATE (nothing
+ *                      changed) when prefix caching needs a decode token's ID that
+ *                      was not given.
+ *   pa_sched_running / pa_sched_waiting  the running (running order) and waiting
+ *                      (queue order) requests; returns the count, fills up to cap.
+ * Not thread-safe: one scheduler thread.
+ */
+typedef struct pa_scheduler pa_scheduler;
+
+typedef struct pa_sched_plan {
+    int64_t step;                       /* steps run before this one */
+    int32_t num_finished, num_arrived, num_admitted, num_preempted;
+    int32_t num_prefill, num_decode, num_decode_cows, num_swapped_in, num_swapped_out;
+    int64_t num_prefill_tokens;
+    const int64_t* finished;            /* [num_finished] */
+    const int64_t* arrived;             /* [num_arrived] */
+    const int64_t* admitted;            /* [num_admitted] */
+    const int32_t* admitted_cached;     /* [num_admitted] prompt tokens already cached */
+    const int64_t* preempted;           /* [num_preempted] recomputed later */
+    const int64_t* prefill_rid;         /* [num_prefill] chunk's request */
+    const int32_t* prefill_start;       /* [num_prefill] its first position */
+    const int32_t* prefill_count;       /* [num_prefill] its tokens */
+    const int64_t* prefill_slots;       /* [num_prefill_tokens] chunk after chunk */
+    const int64_t* decode_rid;          /* [num_decode] */
+    const int64_t* decode_pos;          /* [num_decode] position of the new token */
+    const int64_t* decode_slot;         /* [num_decode] */
+    const int32_t* decode_cow;          /* [num_decode][2] (src, dst), -1 -1 = none */
+    const int64_t* swapped_in;          /* [num_swapped_in] */
+    const int32_t* swapped_in_pairs;    /* [num_swapped_in] pairs of each */
+    const int32_t* swap_in;             /* (host, device) block pairs, request after request */
+    const int64_t* swapped_out;         /* [num_swapped_out] */
+    const int32_t* swapped_out_pairs;   /* [num_swapped_out] */
+    const int32_t* swap_out;            /* (device, host) block pairs */
+} pa_sched_plan;
+
+pa_status pa_sched_create(int32_t num_blocks, int32_t block_size,
+                          const int32_t* initial_free_order, int32_t chunk,
+                          int32_t prefix_caching, int32_t num_host_blocks, pa_scheduler** out);
+void      pa_sched_destroy(pa_scheduler* s);
+pa_allocator* pa_sched_allocator(pa_scheduler* s);
+pa_status pa_sched_add_requests(pa_scheduler* s, int32_t n, const int32_t* prompt_lens,
+                                const int32_t* out_lens, const int32_t* prompt_tokens,
+                                const int32_t* out_tokens, int64_t* rids);
+pa_status pa_sched_push_tokens(pa_scheduler* s, const int64_t* rids, const int32_t* tokens,
+                               int32_t n);
+pa_status pa_sched_step(pa_scheduler* s, pa_sched_plan* plan);
+int32_t   pa_sched_running(const pa_scheduler* s, int64_t* rids, int32_t* prompts,
+                           int32_t* lengths, int32_t cap);
+int32_t   pa_sched_waiting(const pa_scheduler* s, int64_t* rids, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

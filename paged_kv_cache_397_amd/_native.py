@@ -32,6 +32,23 @@ class PagedKVError(RuntimeError):
         super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({_status_string(status)})")
 
 
+class SchedPlan(ctypes.Structure):
+    """pa_sched_plan: counts and pointers into the scheduler's arrays."""
+    _fields_ = [("step", c_i64),
+                ("num_finished", c_i32), ("num_arrived", c_i32), ("num_admitted", c_i32),
+                ("num_preempted", c_i32), ("num_prefill", c_i32), ("num_decode", c_i32),
+                ("num_decode_cows", c_i32), ("num_swapped_in", c_i32), ("num_swapped_out", c_i32),
+                ("num_prefill_tokens", c_i64),
+                ("finished", P_i64), ("arrived", P_i64), ("admitted", P_i64),
+                ("admitted_cached", P_i32), ("preempted", P_i64),
+                ("prefill_rid", P_i64), ("prefill_start", P_i32), ("prefill_count", P_i32),
+                ("prefill_slots", P_i64),
+                ("decode_rid", P_i64), ("decode_pos", P_i64), ("decode_slot", P_i64),
+                ("decode_cow", P_i32),
+                ("swapped_in", P_i64), ("swapped_in_pairs", P_i32), ("swap_in", P_i32),
+                ("swapped_out", P_i64), ("swapped_out_pairs", P_i32), ("swap_out", P_i32)]
+
+
 class CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", c_i32), ("block_size", c_i32), ("num_kv_heads", c_i32),
                 ("head_dim", c_i32), ("dtype", c_i32)]
@@ -91,6 +108,14 @@ SIGNATURES = {
     "pa_seq_is_swapped": (c_i32, [c_vp, c_i64]),
     "pa_seq_swap_out": (c_i32, [c_vp, c_i64, c_vp, c_i32, P_i32]),
     "pa_seq_swap_in": (c_i32, [c_vp, c_i64, c_vp, c_i32, P_i32]),
+    "pa_sched_create": (c_i32, [c_i32, c_i32, c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]),
+    "pa_sched_destroy": (None, [c_vp]),
+    "pa_sched_allocator": (c_vp, [c_vp]),
+    "pa_sched_add_requests": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "pa_sched_push_tokens": (c_i32, [c_vp, c_vp, c_vp, c_i32]),
+    "pa_sched_step": (c_i32, [c_vp, ctypes.POINTER(SchedPlan)]),
+    "pa_sched_running": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32]),
+    "pa_sched_waiting": (c_i32, [c_vp, c_vp, c_i32]),
 }
 
 _lib = None

@@ -32,10 +32,22 @@ class BlockAllocator:
         self.num_blocks = num_blocks
         self.block_size = block_size
 
+    @classmethod
+    def borrowed(cls, handle, num_blocks: int, block_size: int, owner) -> "BlockAllocator":
+        """A handle on an allocator another object owns (a scheduler's); `owner` is
+        kept alive with it, and closing it destroys nothing."""
+        self = cls.__new__(cls)
+        self._lib = N.lib()
+        self._h = ctypes.c_void_p(handle)
+        self._owner = owner
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        return self
+
     def close(self):
-        if self._h:
+        if self._h and getattr(self, "_owner", None) is None:
             self._lib.pa_alloc_destroy(self._h)
-            self._h = None
+        self._h = None
 
     def __del__(self):
         try:
@@ -80,11 +92,18 @@ class BlockAllocator:
         N.check(self._lib.pa_seq_slots(self._h, seq, start, count, _ptr(out)), "seq_slots")
         return out[:count]
 
-    def batch_metadata(self, seqs, max_blocks_per_seq: int):
+    def batch_metadata(self, seqs, max_blocks_per_seq: int, tables=None, ctx=None):
+        """Block tables [n, max_blocks_per_seq] (padding -1) and context lengths [n],
+        into `tables` / `ctx` when given (C-contiguous int32 of those shapes)."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int64)
         n = seqs.shape[0]
-        tables = np.empty((n, max_blocks_per_seq), dtype=np.int32)
-        ctx = np.empty(n, dtype=np.int32)
+        if tables is None:
+            tables = np.empty((n, max_blocks_per_seq), dtype=np.int32)
+        if ctx is None:
+            ctx = np.empty(n, dtype=np.int32)
+        if (tables.shape != (n, max_blocks_per_seq) or tables.dtype != np.int32 or
+                not tables.flags.c_contiguous or ctx.shape != (n,) or ctx.dtype != np.int32):
+            raise ValueError("tables / ctx do not match the batch")
         N.check(self._lib.pa_batch_metadata(self._h, _ptr(seqs), n, max_blocks_per_seq,
                                             _ptr(tables), _ptr(ctx)), "batch_metadata")
         return tables, ctx

@@ -26,7 +26,7 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 PROBE_LIB = os.path.join(PKG, "libpagedkv_probe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "allocator.cpp", "kernels_cache.hip", "kernels_decode.hip",
+SOURCES = ["api.cpp", "allocator.cpp", "scheduler.cpp", "kernels_cache.hip", "kernels_decode.hip",
            "kernels_prefill.hip"]
 # decode_variant.hip is compiled once per decode kernel variant (load policy, decode
 # step, block size 8) so that the variants build in parallel.

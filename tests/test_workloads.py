@@ -32,3 +32,12 @@ def test_config_context_lengths():
     assert list(CONFIGS["tiny_f32"].context_lens()) == [1, 15, 16, 33]
     p = CONFIGS["tiny_f32"].pool_order()
     assert sorted(p) == list(range(16))
+
+
+def test_generated_tokens_vectorised_equals_scalar():
+    """The array form of the counter-based token draw gives the scalar form's IDs,
+    including past 2^32 in the hashed state (large request IDs and positions)."""
+    from workloads import gen
+    for seed, req, first in ((9, 0, 0), (9, 123, 1000), (17, 70000, 1 << 19)):
+        got = gen.generated_tokens(seed, req, first, 64, 64)
+        assert got.tolist() == [gen.generated_token(seed, req, first + k, 64) for k in range(64)]

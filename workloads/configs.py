@@ -126,6 +126,9 @@ class TraceConfig:
     def gen_token(self, rid: int, position: int) -> int:
         return gen.generated_token(self.seed, rid, position, self.vocab)
 
+    def gen_tokens(self, rid: int, first: int, count: int) -> np.ndarray:
+        return gen.generated_tokens(self.seed, rid, first, count, self.vocab)
+
 
 @dataclass(frozen=True)
 class PrefillConfig:

@@ -194,6 +194,19 @@ def generated_token(seed: int, req: int, position: int, vocab: int) -> int:
     return int(x % vocab)
 
 
+def generated_tokens(seed: int, req: int, first: int, count: int, vocab: int) -> np.ndarray:
+    """generated_token for positions first .. first + count - 1, as int32 (the same
+    SplitMix64 output, computed on uint64 arrays)."""
+    with np.errstate(over="ignore"):
+        pos = np.arange(first, first + count, dtype=np.uint64)
+        z = (np.uint64((int(seed) << 48) ^ (TAG_GEN_TOKEN << 40) ^ (int(req) << 20)) ^ pos)
+        z = z + np.uint64(0x9E3779B97F4A7C15)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        z = z ^ (z >> np.uint64(31))
+    return (z % np.uint64(vocab)).astype(np.int32)
+
+
 # ----------------------------------------------------------------------------- full-size serving-trace values
 
 TAG_TRACE_TABLE = 12   # value tables of the full-size trace parity runs
