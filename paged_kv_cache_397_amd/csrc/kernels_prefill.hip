@@ -103,17 +103,20 @@ struct ColState {
 };
 
 // Scores of one pair for the wave's NB query blocks (four independent MFMA chains
-// for NB = 2): S0 for tile 0, S1 for tile 1.
-template <int D, int NB>
+// for NB = 2): S0 for tile 0, S1 for tile 1.  Masked: only the blocks whose bit is
+// set in `act` (uniform) are computed; the others are left as they are.
+template <int D, int NB, bool Masked = false>
 __device__ __forceinline__ void pair_scores(f32x4 (&S0)[NB], f32x4 (&S1)[NB],
                                             const u32x4 (&q)[NB][D / 32],
-                                            const u32x4 (&k0)[D / 32], const u32x4 (&k1)[D / 32]) {
+                                            const u32x4 (&k0)[D / 32], const u32x4 (&k1)[D / 32],
+                                            uint32_t act = ~0u) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) S0[b] = S1[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+            if (Masked && !((act >> b) & 1u)) continue;
             S0[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0[s]),
                                                             __builtin_bit_cast(bf16x8, q[b][s]),
                                                             S0[b], 0, 0, 0);
@@ -136,14 +139,18 @@ __device__ __forceinline__ void pair_scores(f32x4 (&S0)[NB], f32x4 (&S1)[NB],
 // sequence end: per-column masks, and V rows at or past vlim zeroed (they may hold
 // anything, and a zero weight times NaN is NaN).  Otherwise every key is visible to
 // every column.  c >= 0 (scale * log2 e).
-template <int D, int NB, bool kEdge>
+template <int D, int NB, bool kEdge, bool Masked = false>
 __device__ __forceinline__ bool pair_max(const ColState<D> (&st)[NB], float (&x)[NB][8],
                                          float (&mx)[NB], const f32x4 (&S0)[NB],
                                          const f32x4 (&S1)[NB], int key0, const int (&lim)[NB],
-                                         float c, int j) {
+                                         float c, int j, uint32_t act = ~0u) {
     bool any = false;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+        if (Masked && !((act >> b) & 1u)) {
+            mx[b] = kNegInf;  // a block that sees no key of the pair: nothing moves
+            continue;
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             x[b][r] = S0[b][r];
@@ -178,11 +185,12 @@ __device__ __forceinline__ void rescale(ColState<D> (&st)[NB], const float (&mx)
     }
 }
 
-template <int D, int NB>
+template <int D, int NB, bool Masked = false>
 __device__ __forceinline__ void pair_weights(bf16x8 (&pB)[NB], const ColState<D> (&st)[NB],
-                                             const float (&x)[NB][8], float c) {
+                                             const float (&x)[NB][8], float c, uint32_t act = ~0u) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+        if (Masked && !((act >> b) & 1u)) continue;
         uint32_t pw[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -192,9 +200,10 @@ __device__ __forceinline__ void pair_weights(bf16x8 (&pB)[NB], const ColState<D>
     }
 }
 
-template <int D, int NB, bool kEdge>
+template <int D, int NB, bool kEdge, bool Masked = false>
 __device__ __forceinline__ void pair_pv(ColState<D> (&st)[NB], const bf16x8 (&pB)[NB],
-                                        u32x4 (&va)[D / 16], int key0, int vlim, int j) {
+                                        u32x4 (&va)[D / 16], int key0, int vlim, int j,
+                                        uint32_t act = ~0u) {
     constexpr int NG = D / 16;
     // the V operands were read by inline asm the compiler does not track: wait here
 #pragma unroll
@@ -215,14 +224,18 @@ __device__ __forceinline__ void pair_pv(ColState<D> (&st)[NB], const bf16x8 (&pB
         else
             vA = __builtin_bit_cast(bf16x8, va[g]);
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
+            if (Masked && !((act >> b) & 1u)) continue;
             st[b].acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vA, pB[b], st[b].acc[g], 0, 0, 0);
+        }
     }
     const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b) {
+        if (Masked && !((act >> b) & 1u)) continue;
         st[b].lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(one2, one2, one2, one2),
                                                              pB[b], st[b].lsum, 0, 0, 0);
+    }
 }
 
 // Scheduling hints: within the current region, alternate n_mfma groups of one matrix
@@ -457,6 +470,17 @@ void prefill_kernel(PrefillArgs a) {
     // wait for its copies (later pairs' may stay in flight).
     // Pairs below p_fast are unmasked; the last pair is always masked (pf <= np - 1).
     const int pf = min(p_fast, np - 1);
+    // Blocks that see a key of pair p (uniform): block b's last such pair is
+    // (lim_hi[b] - 1) / 32; an empty block (lim_hi = 0) sees none.
+    int last_pair[kQB];
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) last_pair[b] = lim_hi[b] == 0 ? -1 : (lim_hi[b] - 1) / kPairKeys;
+    auto active_at = [&](int pp) -> uint32_t {
+        uint32_t m = 0;
+#pragma unroll
+        for (int b = 0; b < kQB; ++b) m |= (pp <= last_pair[b] ? 1u : 0u) << b;
+        return uni(static_cast<int>(m));
+    };
     f32x4 S0[kQB], S1[kQB];
     float x[kQB][8];
     if (np >= kStages - 1)
@@ -499,23 +523,28 @@ void prefill_kernel(PrefillArgs a) {
         // A.  Near the diagonal or the sequence end every block is masked; a block that
         // sees no key of the pair adds exact zeros (its maximum is already finite:
         // every column sees key 0 in pair 0).
+        // Masked pairs skip the blocks that see no key of the pair (past a block's last
+        // row, or an empty block): a fully masked pair would only add exact zeros.
+        const uint32_t act = kEdge ? active_at(p) : ~0u;
+        const uint32_t act_next = kEdgeNext ? active_at(p + 1) : ~0u;
         bf16x8 pB[kQB];
-        pair_weights<D, kQB>(pB, st, x, cs);
+        pair_weights<D, kQB, kEdge>(pB, st, x, cs, act);
         if constexpr (kNext) {
             // 2 NG V reads were issued after the K reads: at most min(2 NG, 15) LDS reads
             // outstanding leaves every K read done
 #pragma unroll
             for (int k = 0; k < NL; ++k)
                 asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(k0[k]), "+v"(k1[k]) : "i"(2 * NG > 15 ? 15 : 2 * NG));
-            pair_scores<D, kQB>(N0, N1, q, k0, k1);
+            pair_scores<D, kQB, kEdgeNext>(N0, N1, q, k0, k1, act_next);
             interleave_mfma_valu<4 * NL * kQB, 3>();
         }
         // B
-        pair_pv<D, kQB, kEdge>(st, pB, va, p * kPairKeys, L, j);
+        pair_pv<D, kQB, kEdge, kEdge>(st, pB, va, p * kPairKeys, L, j, act);
         if constexpr (kNext) {
             float mx[kQB];
-            const bool any = pair_max<D, kQB, kEdgeNext>(st, x, mx, N0, N1, (p + 1) * kPairKeys,
-                                                         lim, cs, j);
+            const bool any = pair_max<D, kQB, kEdgeNext, kEdgeNext>(st, x, mx, N0, N1,
+                                                                    (p + 1) * kPairKeys, lim, cs,
+                                                                    j, act_next);
             interleave_mfma_valu<(NG + 1) * kQB, 2>();
             if (__ballot(any)) rescale<D, kQB>(st, mx);
         }
