@@ -29,6 +29,13 @@ import time
 
 import numpy as np
 
+# Kernel arguments in device memory instead of host memory (a documented HIP runtime
+# option, read when the runtime starts): the dispatch of each launch then does not
+# fetch its arguments over the host link.  Measured on the batch-256 GQA step:
+# 226.6-227.0 against 230.9-231.2 us/step.  Set before anything starts HIP; a value
+# in the environment wins.
+os.environ.setdefault("HIP_FORCE_DEV_KERNARG", "1")
+
 METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + µs/step, batch 256"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -1288,7 +1295,8 @@ def main():
                    "kv_heads": Hkv, "head_dim": D, "block_size": B, "pool_blocks": cfg.num_blocks,
                    "sum_ctx_first_step": int(tok[0]), "units": units, "seed": cfg.seed,
                    "kv_loads": "cached (shared blocks)" if shared else "streamed (non-temporal)",
-                   "step_launches": 1 if one_launch else 2},
+                   "step_launches": 1 if one_launch else 2,
+                   "hip_force_dev_kernarg": os.environ.get("HIP_FORCE_DEV_KERNARG")},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "shared_prefix_unique": unique,
         "us_per_step": round(wall / steps * 1e6, 2),
