@@ -184,13 +184,17 @@ def cpu_baseline(cfg, ctx, q_host, seconds):
 
 
 def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, units, ws, order,
-                      gtok):
+                      gtok, overlap=False):
     """The trace as a serving loop: each step the host plans it with a fresh library
     scheduler, writes its metadata into a pinned ring slot, uploads the slot with
     one copy and launches the step's kernels; the device runs behind the host, so
     the host's planning of step n + 1 overlaps the device's step n.  Returns the
     device timeline per step (events at step `lo` and after the last step: host
-    bubbles included) and the host's own time per step."""
+    bubbles included) and the host's own time per step.  overlap: a step's prompt
+    phase (chunk writes and prefill attention) runs on a second stream beside its
+    decode phase (token writes and decode attention) - they touch disjoint blocks
+    and sequences - and the two join before the next step, whose work may depend on
+    either (a finished request's blocks reused, a completed prompt decoding)."""
     import torch
     from paged_kv_cache_397_amd import ops
     from paged_kv_cache_397_amd.scheduler import TraceScheduler
@@ -224,6 +228,7 @@ def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, u
     dev_views = {n: dev[a:a + c * np.dtype(t).itemsize].view(tdt[t]) for n, (a, t, c) in offs.items()}
     ring_ev = [None] * ring
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if overlap else stream  # default priority
     lo = min(50, cfg.steps - 1)
     ev_lo, ev_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     host_s, wait_s = [], []
@@ -260,11 +265,15 @@ def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, u
         ev.record(stream)
         ring_ev[k] = ev
         if P:
-            ops.reshape_and_cache(spec, pool["pk"][:P], pool["pv"][:P], dev_views["pslots"][:P], kc, vc)
-            ops.paged_attn_prefill(spec, pout[:P], pool["pq"][:P], kc, vc,
-                                   dev_views["ptables"][:C * max_blocks].view(C, max_blocks),
-                                   dev_views["pqs"][:C + 1], dev_views["pctx"][:C], cfg.scale,
-                                   max_query_len=int(plan.prefill_count.max()))
+            if overlap:
+                side.wait_stream(stream)  # the upload, and every earlier step
+            with torch.cuda.stream(side):
+                ops.reshape_and_cache(spec, pool["pk"][:P], pool["pv"][:P], dev_views["pslots"][:P],
+                                      kc, vc)
+                ops.paged_attn_prefill(spec, pout[:P], pool["pq"][:P], kc, vc,
+                                       dev_views["ptables"][:C * max_blocks].view(C, max_blocks),
+                                       dev_views["pqs"][:C + 1], dev_views["pctx"][:C], cfg.scale,
+                                       max_query_len=int(plan.prefill_count.max()))
         if S:
             ops.append_tokens(spec, pool["k"][:S], pool["v"][:S], dev_views["dslots"][:S], kc, vc,
                               cow_pairs=(dev_views["cows"][:2 * S].view(S, 2)
@@ -273,6 +282,8 @@ def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, u
                                   dev_views["tables"][:S * max_blocks].view(S, max_blocks),
                                   dev_views["ctx"][:S], cfg.scale, units, ws,
                                   keep_cached=bool(cfg.prefix))
+        if overlap and P:
+            stream.wait_stream(side)  # join before the next step
         host_s.append(time.perf_counter() - h0)
     ev_end.record(stream)
     torch.cuda.synchronize()
@@ -282,7 +293,9 @@ def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, u
     hs = np.array(host_s[lo:]) * 1e6 - ws_
     return {"note": "a fresh scheduler plans each step while the device runs the previous ones; "
                     "one pinned-to-device copy of the step's metadata per step; device timeline "
-                    "from step %d to the end over the steps, host bubbles included" % lo,
+                    "from step %d to the end over the steps, host bubbles included" % lo
+                    + ("; prompt and decode phases of a step on two streams, joined per step"
+                       if overlap else ""),
             "us_per_step": round(float(per), 2),
             "host_us_per_step": {"mean": round(float(hs.mean()), 2),
                                  "p99": round(float(np.percentile(hs, 99)), 2),
@@ -422,6 +435,8 @@ def run_trace(args):
     torch.cuda.empty_cache()
     e2e = _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax_all, smax_all, cmax_all,
                             units, ws, order, gtok)
+    e2e_ov = _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax_all, smax_all,
+                               cmax_all, units, ws, order, gtok, overlap=True)
     pflops = np.array([d.get("pflops", 0.0) for d in steps_dev])
     kv_tok = 2 * Hkv * D * spec_elem_bytes(cfg.dtype)
     kv_bytes = np.array([d["ctx_sum"] for d in steps_dev], dtype=np.float64) * kv_tok
@@ -467,6 +482,7 @@ def run_trace(args):
                                  round(float(np.mean(host_s[:model_steps])) * 1e6, 2)},
         "wall_ms_all_steps": round(wall * 1e3, 2),
         "end_to_end": e2e,
+        "end_to_end_phases_overlapped": e2e_ov,
     }
     print(json.dumps(result), flush=True)
 

@@ -138,3 +138,97 @@ def test_trace_with_swap_preemption_matches_oracle():
         decoded += S
     assert swapped > 0 and swapped_back > 0, (swapped, swapped_back)
     assert decoded > 300
+
+
+def test_trace_with_prompt_and_decode_phases_on_two_streams():
+    """A step's prompt phase (chunk writes, then prefill attention over the chunks) on a
+    second stream beside its decode phase (token writes, decode attention), the two
+    joined before the next step, as the serving-trace bench overlaps them: every
+    prefill row and every decoded sequence of every step matches the fp64 oracle.
+    The phases touch disjoint sequences and blocks; the join orders a step after
+    everything the previous one wrote (a finished request's blocks reused, a
+    completed prompt decoding)."""
+    from oracle.attention import prefill_attention
+    from oracle.layout import to_float64 as f64
+    Hq, Hkv = 8, 4
+    cfg = CONFIGS["trace_small"]
+    B, D, dtype = cfg.block_size, cfg.head_dim, cfg.dtype
+    spec = ops.CacheSpec(cfg.num_blocks, B, Hkv, D, dtype)
+    kc, vc = ops.empty_cache(spec)
+    kc.fill_(float("nan"))
+    vc.fill_(float("nan"))
+    sched = TraceScheduler(cfg.num_blocks, B, cfg.chunk, gen.pool_permutation(cfg.seed, cfg.num_blocks))
+    max_blocks = -(-(cfg.prompt_hi + cfg.out_hi) // B)
+    scale = 1 / math.sqrt(D)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    both = 0
+    for n in range(cfg.steps):
+        p, o = gen.trace_arrivals(cfg.seed, n, cfg.arrival_mean, cfg.prompt_lo, cfg.prompt_hi,
+                                  cfg.out_p, cfg.out_lo, cfg.out_hi)
+        plan = sched.step(n, list(zip(p.tolist(), o.tolist())))
+        S, C = len(plan.decode_rids), len(plan.prefill)
+        # inputs, uploaded on the main stream before the fork
+        if C:
+            ks, vs, sl, qs = [], [], [], []
+            for rid, start, count, slots in plan.prefill:
+                k, v = gen.trace_token_kv(cfg.seed, rid, range(start, start + count), Hkv, D, dtype)
+                ks.append(k), vs.append(v), sl.append(slots)
+                qs.append(np.stack([gen.trace_query(cfg.seed, rid, start + i, Hq, D, dtype)
+                                    for i in range(count)]))
+            pk, pv = to_device(np.concatenate(ks), spec), to_device(np.concatenate(vs), spec)
+            pq_host = np.concatenate(qs)
+            pq = to_device(pq_host, spec)
+            pslots = torch.from_numpy(np.concatenate(sl)).cuda()
+            counts = np.array([c for _, _, c, _ in plan.prefill], dtype=np.int64)
+            starts = np.array([s for _, s, _, _ in plan.prefill], dtype=np.int64)
+            pqs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+            pctx = torch.from_numpy((starts + counts).astype(np.int32)).cuda()
+            ptab, _ = sched.alloc.batch_metadata(plan.prefill_rids, max_blocks)
+            ptab = torch.from_numpy(ptab).cuda()
+            pout = torch.full((int(counts.sum()), Hq, D), float("nan"), dtype=spec.torch_dtype,
+                              device="cuda")
+        if S:
+            kv = [gen.trace_token_kv(cfg.seed, int(r), [int(q)], Hkv, D, dtype)
+                  for r, q in zip(plan.decode_rids, plan.decode_pos)]
+            dk = to_device(np.concatenate([a for a, _ in kv]), spec)
+            dv = to_device(np.concatenate([b for _, b in kv]), spec)
+            dslots = torch.from_numpy(plan.decode_slots).cuda()
+            cows = torch.from_numpy(np.ascontiguousarray(plan.decode_cows)).cuda()
+            tables, ctx = sched.alloc.batch_metadata(plan.decode_rids, max_blocks)
+            q_host = np.stack([gen.trace_query(cfg.seed, int(r), int(q), Hq, D, dtype)
+                               for r, q in zip(plan.decode_rids, plan.decode_pos)])
+            dq = to_device(q_host, spec)
+            dtab, dctx = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+            out = torch.full((S, Hq, D), float("nan"), dtype=spec.torch_dtype, device="cuda")
+        # the two phases
+        if C:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                ops.reshape_and_cache(spec, pk, pv, pslots, kc, vc)
+                ops.paged_attn_prefill(spec, pout, pq, kc, vc, ptab, pqs, pctx, scale,
+                                       max_query_len=int(counts.max()))
+        if S:
+            ops.append_tokens(spec, dk, dv, dslots, kc, vc, cow_pairs=cows)
+            ops.paged_attn_decode(spec, out, dq, kc, vc, dtab, dctx, scale, num_units=37)
+        if C:
+            main.wait_stream(side)
+        torch.cuda.synchronize()
+        both += bool(C and S)
+        if C:
+            got = to_float64(to_storage(pout), dtype)
+            o0 = 0
+            for rid, start, count, _ in plan.prefill:
+                K, V = gen.trace_token_kv(cfg.seed, rid, range(start + count), Hkv, D, dtype)
+                ref = prefill_attention(f64(pq_host[o0:o0 + count], dtype), f64(K, dtype),
+                                        f64(V, dtype), scale, start)
+                assert_close(got[o0:o0 + count], ref, dtype, f"step {n} prefill of {rid}")
+                o0 += count
+        if S:
+            got = to_float64(to_storage(out), dtype)
+            ref = []
+            for i, (r, q) in enumerate(zip(plan.decode_rids, plan.decode_pos)):
+                K, V = gen.trace_token_kv(cfg.seed, int(r), range(int(q) + 1), Hkv, D, dtype)
+                ref.append(contiguous_decode(q_host[i], K, V, scale, dtype))
+            assert_close(got, np.stack(ref), dtype, f"step {n} decode")
+    assert both > 10, "steps with both phases were meant to be common"
