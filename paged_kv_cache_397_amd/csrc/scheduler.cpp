@@ -279,6 +279,9 @@ pa_status pa_sched_add_requests(pa_scheduler* s, int32_t n, const int32_t* promp
     for (int32_t k = 0; k < n; ++k)
         if (prompt_lens[k] < 0 || out_lens[k] < 0) return PA_ERR_INVALID_ARG;
     const size_t base = s->reqs.size();
+    // all or nothing: every request is built before any is queued
+    std::vector<std::unique_ptr<Req>> made;
+    made.reserve(static_cast<size_t>(n));
     int64_t pt = 0, ot = 0;
     for (int32_t k = 0; k < n; ++k) {
         std::unique_ptr<Req> r(new (std::nothrow) Req());
@@ -293,9 +296,12 @@ pa_status pa_sched_add_requests(pa_scheduler* s, int32_t n, const int32_t* promp
         }
         pt += prompt_lens[k];
         ot += out_lens[k];
-        if (rids) rids[k] = r->rid;
-        s->pending.push_back(r.get());
-        s->reqs.push_back(std::move(r));
+        made.push_back(std::move(r));
+    }
+    for (int32_t k = 0; k < n; ++k) {
+        if (rids) rids[k] = made[static_cast<size_t>(k)]->rid;
+        s->pending.push_back(made[static_cast<size_t>(k)].get());
+        s->reqs.push_back(std::move(made[static_cast<size_t>(k)]));
     }
     return PA_OK;
 }

@@ -169,9 +169,23 @@ class TraceScheduler:
         prompts = [np.asarray(p, dtype=np.int32) for p, _ in arrivals]
         plens = np.fromiter((len(p) for p in prompts), dtype=np.int32, count=n)
         ptoks = np.concatenate(prompts) if n else np.zeros(0, dtype=np.int32)
-        otoks = (np.concatenate([self._outputs(rid0 + k, int(plens[k]), int(outs[k])) for k in range(n)])
-                 if n else np.zeros(0, dtype=np.int32))
+        outs_tok = [self._outputs(rid0 + k, int(plens[k]), int(outs[k])) for k in range(n)]
+        if all(o.size == 0 for o in outs_tok):
+            otoks = None  # a live loop: token IDs come later, through push_tokens
+        elif all(o.size == int(outs[k]) for k, o in enumerate(outs_tok)):
+            otoks = np.concatenate(outs_tok)
+        else:
+            raise ValueError("the token source must give each request all of its outputs, or none")
         return Arrivals(plens, outs, ptoks, otoks)
+
+    def push_tokens(self, rids, tokens) -> None:
+        """Pass sampled token IDs (one per named request, in order) to the scheduler."""
+        r = np.ascontiguousarray(rids, dtype=np.int64)
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        if r.shape != t.shape:
+            raise ValueError("one token per request")
+        N.check(self._lib.pa_sched_push_tokens(self._h, _ptr(r), _ptr(t), int(r.shape[0])),
+                "pa_sched_push_tokens")
 
     def add_requests(self, arrivals) -> list[int]:
         """Queue arrivals (pairs or packed) for the next step; returns their IDs."""

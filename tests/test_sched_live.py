@@ -43,6 +43,14 @@ def test_argument_checks():
         lib.pa_sched_destroy(h)
 
 
+def test_partial_token_source_is_refused():
+    """A token source that gives some requests fewer outputs than they generate would
+    leave the scheduler reading past the tokens given: the binding refuses it."""
+    s = TraceScheduler(8, 4, 4, gen_tokens=lambda rid, first, count: np.zeros(min(count, 1), dtype=np.int32))
+    with pytest.raises(ValueError):
+        s.add_requests([(np.arange(6, dtype=np.int32), 2)])
+
+
 def test_missing_decode_token_changes_nothing():
     """A request whose next token ID was never given: the step fails before any
     change, and runs as planned once the token is pushed."""
@@ -56,9 +64,7 @@ def test_missing_decode_token_changes_nothing():
         s.step(2, [])                                     # decodes position 6: no ID
     assert e.value.status == N.PA_ERR_STATE
     assert s.alloc.free_list() == free_before and s.alloc.length(0) == 6
-    N.check(s._lib.pa_sched_push_tokens(s._h, np.array([0], dtype=np.int64).ctypes.data_as(ctypes.c_void_p),
-                                         np.array([7], dtype=np.int32).ctypes.data_as(ctypes.c_void_p), 1),
-            "push")
+    s.push_tokens([0], [7])
     assert _events(s.step(2, [])) == _events(ref.step(2, []))
 
 
@@ -89,9 +95,7 @@ def test_live_token_push_equals_replay(num_blocks, host):
             if need:
                 ids = np.array(need, dtype=np.int64)
                 toks = np.array([cfg.gen_token(r, prompt[r] + gen_count[r]) for r in need], dtype=np.int32)
-                N.check(live._lib.pa_sched_push_tokens(live._h, ids.ctypes.data_as(ctypes.c_void_p),
-                                                       toks.ctypes.data_as(ctypes.c_void_p), len(need)),
-                        "push")
+                live.push_tokens(ids, toks)
                 for r in need:
                     known[r] += 1
         a = live.step(n, arr)
