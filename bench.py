@@ -811,6 +811,45 @@ def run_blocksize(args):
                   "table_entries": int(S * tables.shape[1])}
         del kc, vc
         torch.cuda.empty_cache()
+    # chunked prefill at each block size: the prefill_13b batch (8 chunks of 512 tokens
+    # after U[0, 3584] cached tokens), the same pool tokens at every B
+    pc = CONFIGS["prefill_13b"]
+    offsets = pc.offsets()
+    Lp = (offsets + pc.chunk).astype(np.int32)
+    flops = prefill_flops(offsets, pc.chunk, pc.num_q_heads, pc.head_dim)
+    pre = {}
+    for B in (8, 16, 32, 64):
+        N = pc.num_blocks * 16 // B
+        spec = ops.CacheSpec(N, B, pc.num_kv_heads, pc.head_dim, "bf16")
+        kc, vc = ops.empty_cache(spec)
+        kc.normal_()
+        vc.normal_()
+        alloc = BlockAllocator(N, B, gen.pool_permutation(pc.seed, N))
+        for i in range(pc.num_seqs):
+            alloc.add(i, int(Lp[i]))
+        tables, _ = alloc.batch_metadata(np.arange(pc.num_seqs), -(-int(Lp.max()) // B))
+        t_dev = torch.from_numpy(tables).cuda()
+        T = pc.num_seqs * pc.chunk
+        q = torch.randn(T, pc.num_q_heads, pc.head_dim, device="cuda").to(torch.bfloat16)
+        out = torch.empty_like(q)
+        qs = torch.arange(0, T + 1, pc.chunk, dtype=torch.int32, device="cuda")
+        c_dev = torch.from_numpy(Lp).cuda()
+        call = lambda: ops.paged_attn_prefill(spec, out, q, kc, vc, t_dev, qs, c_dev, pc.scale,
+                                              max_query_len=pc.chunk, stream=stream)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(args.steps, 10)
+        a.record(stream)
+        for _ in range(reps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3 / reps
+        pre[B] = {"prefill_us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1)}
+        del kc, vc
+        torch.cuda.empty_cache()
     result = {
         "metric": "KV utilisation by block size (paged vs contiguous max-length reservation) "
                   "and decode attention us by block size",
@@ -821,9 +860,10 @@ def run_blocksize(args):
         "data": "synthetic",
         "config": {"workload": f"blocksize_sweep: {tr.name} ({tr.title}) steps 50..{tr.steps - 1}, "
                                f"pool {pool_tokens} tokens; decode on {dc.name}",
-                   "contiguous_max_new": tr.out_hi},
+                   "contiguous_max_new": tr.out_hi, "prefill_batch": pc.name},
         "utilisation": {str(k): v for k, v in util.items()},
         "decode": {str(k): v for k, v in dec.items()},
+        "prefill": {str(k): v for k, v in pre.items()},
         "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)

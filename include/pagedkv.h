@@ -49,9 +49,8 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
  * ([P1] section 2.2: fixed-size pages scattered through one pool; [P2]
  * PagedAttention > 工作原理 > 1. 页表管理: a per-sequence page table).
  *
- * Supported: block_size in {8, 16, 32, 64} (8: every entry point but
- * pa_paged_attn_prefill, which returns PA_ERR_UNSUPPORTED); head_dim in
- * {64, 128}; dtype in {F32, BF16}.  Smaller blocks waste fewer slots at
+ * Supported: block_size in {8, 16, 32, 64}; head_dim in {64, 128}; dtype in
+ * {F32, BF16}.  Smaller blocks waste fewer slots at
  * sequence ends but mean more table entries per token ([P1] section 3.4 on
  * --block-size).
  *

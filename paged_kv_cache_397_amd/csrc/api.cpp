@@ -489,8 +489,6 @@ pa_status pa_paged_attn_prefill(const pa_cache_desc* d, void* out, const void* q
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
     const int32_t group = num_q_heads / d->num_kv_heads;
     if (d->dtype != PA_DTYPE_BF16 || 16 % group != 0) return PA_ERR_UNSUPPORTED;
-    // the prefill kernel stages 16-token tiles of one block each
-    if (d->block_size < pkv::kTile) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
     if (max_blocks_per_seq == 0) return PA_ERR_INVALID_ARG;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
@@ -498,7 +496,7 @@ pa_status pa_paged_attn_prefill(const pa_cache_desc* d, void* out, const void* q
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(query_start, 4) || !aligned(context_lens, 4))
         return PA_ERR_INVALID_ARG;
-    const int32_t tpb = d->block_size / pkv::kTile;
+    const int32_t tpb = d->block_size >= pkv::kTile ? d->block_size / pkv::kTile : 1;
     // int32 in the kernel: cache tile indices, positions, and the workgroup count
     // (at most (num_seqs * Hkv + 7) * (max_query_len / 8 + 1))
     if (static_cast<double>(d->num_blocks) * d->num_kv_heads * tpb >= 2147483647.0 ||
@@ -523,6 +521,7 @@ pa_status pa_paged_attn_prefill(const pa_cache_desc* d, void* out, const void* q
     a.num_blocks = d->num_blocks;
     a.qgroups = 0;
     a.num_groups = 0;
+    a.block_size = d->block_size;
     a.scale_log2e = scale * 1.4426950408889634f;
     return from_hip(pkv::launch_prefill(d->head_dim, group, max_query_len, a,
                                         static_cast<hipStream_t>(stream)));

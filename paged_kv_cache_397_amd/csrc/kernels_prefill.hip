@@ -251,7 +251,10 @@ __device__ __forceinline__ void interleave_mfma_valu() {
     }
 }
 
-template <int D, int G>
+// Half: blocks of 8 tokens; a 16-token tile is copied from two blocks (tokens 0..7
+// of K and key quads 0..1 of V from the first, the rest from the second), so LDS
+// holds the same 16-token tiles either way.
+template <int D, int G, bool Half>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
     constexpr int NL = D / 32;                 // 16-B loads per lane per tile (K and V)
@@ -319,7 +322,7 @@ void prefill_kernel(PrefillArgs a) {
     const int c = r1 - r0;
     const int qb0 = qg * (kWaves * kQB);       // the workgroup's first query block
     if (r0 < 0 || r1 > a.num_tokens || c <= 0 || qb0 * TB >= c) return;  // uniform
-    const int cap = a.max_blocks * a.tiles_per_block * kTile;
+    const int cap = a.max_blocks * a.block_size;
     const int L = min(max(Lraw, 0), cap);
     const int start = L - c;  // position of the chunk's first token (>= 0 for valid input)
 
@@ -365,32 +368,43 @@ void prefill_kernel(PrefillArgs a) {
     const int np = (lim_wg + kPairKeys - 1) / kPairKeys;
     const int nt = (lim_wg + kTile - 1) / kTile;  // tiles holding a visible key
 
-    // Block ids of tiles, 64 at a time: lane k of a window holds the block of tile
-    // base + k.  Window 0 is read here; window w + 1 is copied by wave 0 into an LDS
-    // ring when window w comes into use, 32 pairs before it is needed, so its copy
-    // is covered by the pair loop's waits and barriers like the K/V copies.
+    // Block ids of tiles, WT tiles at a time: lane k of a window holds the block of
+    // tile base + k (Half: table entry 2 base + k, the two blocks of tiles base ..
+    // base + 31).  Window 0 is read here; window w + 1 is copied by wave 0 into an
+    // LDS ring when window w comes into use, WT / 2 pairs before it is needed, so its
+    // copy is covered by the pair loop's waits and barriers like the K/V copies.
+    constexpr int WT = Half ? kWave / 2 : kWave;
     const int tpb = a.tiles_per_block;
     const int32_t* bt = a.block_tables + static_cast<size_t>(s) * a.max_blocks;
+    const int last_entry = max((L - 1) >> 3, 0);  // Half: the sequence's last block
     __shared__ int win_lds[2][kWave];
     auto win_src = [&](int base) -> const int32_t* {
-        const int t = base + lane;
-        return bt + (t < nt ? t / tpb : 0);  // past the visible tiles: any valid tile, never weighted
+        if constexpr (Half) {
+            // the second block of a tile the sequence ends before reads the first again
+            const int e = 2 * base + lane;
+            return bt + (e < 2 * nt ? min(e, last_entry) : 0);
+        } else {
+            const int t = base + lane;
+            return bt + (t < nt ? t / tpb : 0);  // past the visible tiles: any valid tile, never weighted
+        }
     };
     auto copy_window = [&](int base) {
         if (wv == 0)
             __builtin_amdgcn_global_load_lds(
                 (const void __attribute__((address_space(1)))*)win_src(base),
-                (void __attribute__((address_space(3)))*)&win_lds[(base / kWave) & 1][0], 4, 0, 0);
+                (void __attribute__((address_space(3)))*)&win_lds[(base / WT) & 1][0], 4, 0, 0);
     };
-    // lane's tile base + lane: block id -> the tile's index in the cache (once per window)
+    // lane's tile base + lane (Half: lane's block): block id -> the tile's index in
+    // the cache (once per window)
     auto tile_offset = [&](int blk, int base) -> int {
         blk = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
+        if constexpr (Half) return blk * a.num_kv_heads + h;
         return (blk * tpb + (base + lane) % tpb) * a.num_kv_heads + h;
     };
     const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
     const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
     int w_cur = tile_offset(*win_src(0), 0);
-    if (2 * np > kWave) copy_window(kWave);
+    if (2 * np > WT) copy_window(WT);
     // Thread tid copies chunks r * 256 + tid of the pair straight from the cache into
     // LDS (global_load_lds: lane l of a wave lands 16 bytes at the wave's LDS base +
     // 16 l); region (chunk / REGION) is K t0, V t0, K t1, V t1, the same for every
@@ -398,12 +412,12 @@ void prefill_kernel(PrefillArgs a) {
     // the pair loop waits for them explicitly (vmcnt) before its barrier.
     auto issue = [&](int p) {
         const int t0 = 2 * p;
-        if (t0 > 0 && (t0 & (kWave - 1)) == 0) {
+        if (t0 > 0 && (t0 & (WT - 1)) == 0) {
             int raw;
             asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                         : "=v"(raw) : "v"(lds_addr(&win_lds[(t0 / kWave) & 1][lane])));
+                         : "=v"(raw) : "v"(lds_addr(&win_lds[(t0 / WT) & 1][lane])));
             w_cur = tile_offset(raw, t0);
-            if (t0 + kWave < 2 * np) copy_window(t0 + kWave);
+            if (t0 + WT < 2 * np) copy_window(t0 + WT);
         }
         u32x4* stage = lds[p & (kStages - 1)];
 #pragma unroll
@@ -411,11 +425,34 @@ void prefill_kernel(PrefillArgs a) {
             // this wave's 64 chunks of copy r: rw .. rw + 63, all in one region
             const int rw = r * kThreads + wv * kWave;
             const int reg = r * (kThreads / REGION) + (wv * kWave) / REGION;
-            const int toff = __builtin_amdgcn_readlane(w_cur, (t0 + (reg >> 1)) & (kWave - 1));
-            const u32x4* src = ((reg & 1) ? vc : kc) + static_cast<size_t>(toff) * REGION;
-            __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(src + (rw & (REGION - 1)) + lane),
-                (void __attribute__((address_space(3)))*)(stage + rw), 16, 0, 0);
+            if constexpr (Half) {
+                // chunk cidx of the 16-token tile: K (token cidx % 16, dims chunk cidx / 16)
+                // sits in block token / 8; V (quad (cidx / 16) % 4) in block quad / 2
+                constexpr int HALF = REGION / 2;
+                const int t = t0 + (reg >> 1);
+                const int toffA = __builtin_amdgcn_readlane(w_cur, (2 * t) & (kWave - 1));
+                const int toffB = __builtin_amdgcn_readlane(w_cur, (2 * t + 1) & (kWave - 1));
+                const int cidx = (rw & (REGION - 1)) + lane;
+                const u32x4* src;
+                if (reg & 1) {
+                    const int jq = (cidx >> 4) & 3;
+                    src = vc + static_cast<size_t>(jq < 2 ? toffA : toffB) * HALF +
+                          ((cidx >> 6) * 2 + (jq & 1)) * 16 + (cidx & 15);
+                } else {
+                    const int tok = cidx & 15;
+                    src = kc + static_cast<size_t>(tok < 8 ? toffA : toffB) * HALF +
+                          (cidx >> 4) * 8 + (tok & 7);
+                }
+                __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                                 (void __attribute__((address_space(3)))*)(stage + rw),
+                                                 16, 0, 0);
+            } else {
+                const int toff = __builtin_amdgcn_readlane(w_cur, (t0 + (reg >> 1)) & (kWave - 1));
+                const u32x4* src = ((reg & 1) ? vc : kc) + static_cast<size_t>(toff) * REGION;
+                __builtin_amdgcn_global_load_lds(
+                    (const void __attribute__((address_space(1)))*)(src + (rw & (REGION - 1)) + lane),
+                    (void __attribute__((address_space(3)))*)(stage + rw), 16, 0, 0);
+            }
         }
     };
 
@@ -578,17 +615,17 @@ void prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int D>
+template <int D, bool Half>
 hipError_t launch_group_size(int group, PrefillArgs& a, hipStream_t st) {
     const dim3 block(kThreads);
     const int nsh = a.num_seqs * a.num_kv_heads;
     const dim3 grid(kXcds * ((nsh + kXcds - 1) / kXcds) * a.qgroups);
     switch (group) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, block, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<D, 8>), grid, block, 0, st, a); break;
-        case 16: hipLaunchKernelGGL((prefill_kernel<D, 16>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, Half>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, Half>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, Half>), grid, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, Half>), grid, block, 0, st, a); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<D, 16, Half>), grid, block, 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -604,8 +641,13 @@ hipError_t launch_prefill(int head_dim, int group, int max_query_len, PrefillArg
     a.qgroups = (qblocks + kWaves * kQB - 1) / (kWaves * kQB);
     a.num_groups = a.num_seqs * a.num_kv_heads * a.qgroups;
     if (a.num_groups == 0) return hipSuccess;
-    if (head_dim == 128) return launch_group_size<128>(group, a, stream);
-    if (head_dim == 64) return launch_group_size<64>(group, a, stream);
+    const bool half = a.block_size == 8;
+    if (head_dim == 128)
+        return half ? launch_group_size<128, true>(group, a, stream)
+                    : launch_group_size<128, false>(group, a, stream);
+    if (head_dim == 64)
+        return half ? launch_group_size<64, true>(group, a, stream)
+                    : launch_group_size<64, false>(group, a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -75,6 +75,7 @@ struct PrefillArgs {
     int32_t qgroups;              // workgroups per (sequence, KV head)
     int32_t num_groups;           // num_seqs * num_kv_heads * qgroups
     float scale_log2e;
+    int32_t block_size;
 };
 
 constexpr int kRecInts = 8;  // per-unit record: row, seq, first unit, last unit of the split ending there

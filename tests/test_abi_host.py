@@ -136,7 +136,6 @@ def test_prefill_argument_checks_without_a_gpu():
     assert lib.pa_paged_attn_prefill(*args(f32, 4)) == S            # no fp32 prefill kernel
     assert lib.pa_paged_attn_prefill(*args(bf16, 6)) == S           # G = 3 does not divide 16
     assert lib.pa_paged_attn_prefill(*args(bf16, 64)) == S          # G = 32
-    assert lib.pa_paged_attn_prefill(*args(N.CacheDesc(64, 8, 2, 64, 1), 4)) == S  # blocks of 8
     assert lib.pa_paged_attn_prefill(*args(bf16, 5)) == N.PA_ERR_INVALID_ARG  # Hq % Hkv != 0
     assert lib.pa_paged_attn_prefill(*args(bf16, 4, T=-1)) == N.PA_ERR_INVALID_ARG
     assert lib.pa_paged_attn_prefill(*args(bf16, 4, mql=-1)) == N.PA_ERR_INVALID_ARG

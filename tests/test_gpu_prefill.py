@@ -72,7 +72,7 @@ RAGGED = [(1, 1), (40, 40), (300, 77), (16, 16), (700, 129), (33, 1), (7, 0), (5
 
 @pytest.mark.parametrize("D,Hq,Hkv,B", [(128, 32, 8, 16), (128, 16, 16, 16), (64, 16, 8, 16),
                                         (128, 32, 4, 32), (128, 16, 1, 16), (64, 8, 8, 64),
-                                        (128, 8, 4, 16)])
+                                        (128, 8, 4, 16), (128, 32, 8, 8), (64, 16, 16, 8)])
 def test_prefill_matches_oracle(D, Hq, Hkv, B):
     spec = ops.CacheSpec(num_blocks=640, block_size=B, num_kv_heads=Hkv, head_dim=D, dtype="bf16")
     b = Chunks(spec, RAGGED, Hq, seed=41, free_order=gen.pool_permutation(41, 640))
