@@ -223,9 +223,14 @@ def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, u
     pinned = [torch.empty(slot_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(ring)]
     host_views = [{n: p.numpy()[a:a + c * np.dtype(t).itemsize].view(t) for n, (a, t, c) in offs.items()}
                   for p in pinned]
-    dev = torch.empty(slot_bytes, dtype=torch.uint8, device="cuda")
+    # two device staging buffers: step n + 1's upload (on a copy stream) overlaps step
+    # n's kernels, and waits only for step n - 1's, the last user of its buffer
+    devs = [torch.empty(slot_bytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
     tdt = {np.int64: torch.int64, np.int32: torch.int32}
-    dev_views = {n: dev[a:a + c * np.dtype(t).itemsize].view(tdt[t]) for n, (a, t, c) in offs.items()}
+    dev_viewss = [{n: d[a:a + c * np.dtype(t).itemsize].view(tdt[t]) for n, (a, t, c) in offs.items()}
+                  for d in devs]
+    copy_stream = torch.cuda.Stream()  # default priority
+    done_ev = [None, None]
     ring_ev = [None] * ring
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream() if overlap else stream  # default priority
@@ -260,10 +265,16 @@ def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, u
             sched.alloc.batch_metadata(plan.decode_rids, max_blocks,
                                        tables=hv["tables"][:S * max_blocks].reshape(S, max_blocks),
                                        ctx=hv["ctx"][:S])
-        dev.copy_(pinned[k], non_blocking=True)
+        bsel = n & 1
+        dev_views = dev_viewss[bsel]
+        if done_ev[bsel] is not None:
+            copy_stream.wait_event(done_ev[bsel])
+        with torch.cuda.stream(copy_stream):
+            devs[bsel].copy_(pinned[k], non_blocking=True)
         ev = torch.cuda.Event()
-        ev.record(stream)
+        ev.record(copy_stream)
         ring_ev[k] = ev
+        stream.wait_event(ev)
         if P:
             if overlap:
                 side.wait_stream(stream)  # the upload, and every earlier step
@@ -284,6 +295,9 @@ def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, u
                                   keep_cached=bool(cfg.prefix))
         if overlap and P:
             stream.wait_stream(side)  # join before the next step
+        dv = torch.cuda.Event()
+        dv.record(stream)
+        done_ev[bsel] = dv
         host_s.append(time.perf_counter() - h0)
     ev_end.record(stream)
     torch.cuda.synchronize()
@@ -292,7 +306,8 @@ def _trace_end_to_end(cfg, spec, kc, vc, packed, max_blocks, pmax, smax, cmax, u
     ws_ = np.array(wait_s[lo:]) * 1e6
     hs = np.array(host_s[lo:]) * 1e6 - ws_
     return {"note": "a fresh scheduler plans each step while the device runs the previous ones; "
-                    "one pinned-to-device copy of the step's metadata per step; device timeline "
+                    "one pinned-to-device copy of the step's metadata per step, on a copy stream "
+                    "ahead of the kernels (two device staging buffers); device timeline "
                     "from step %d to the end over the steps, host bubbles included" % lo
                     + ("; prompt and decode phases of a step on two streams, joined per step"
                        if overlap else ""),
