@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--step-launch", choices=["one", "two"], default="two",
                     help="a decode step as one launch (pa_decode_step: cache writes folded into "
                          "the decode kernel) or as two (pa_append_tokens, then pa_paged_attn_decode)")
+    ap.add_argument("--metadata", choices=["pinned", "upload"], default="pinned",
+                    help="the write kernel reads a step's metadata from its pinned ring slot in "
+                         "place, or from a device copy uploaded ahead on a copy stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -1158,6 +1161,14 @@ def main():
     R, EV_EVERY = 8, 4
     words = S * 2 + S + 3 * S + 2 * S  # int32 words: slots (int64), ctx, updates, cow pairs
     pin = [torch.empty(words, dtype=torch.int32, pin_memory=True) for _ in range(R)]
+    upload = args.metadata == "upload"
+    # upload: each slot also has a device copy, filled on a copy stream as soon as the
+    # host has staged it (the host runs steps ahead, so the copy is done before the
+    # device reaches the step); the write kernel then reads device memory.  Device
+    # slot n % R is free again once the ring event covering step n - R has completed,
+    # which the host checks before staging; the compute stream waits for each copy.
+    dmeta = [torch.empty(words, dtype=torch.int32, device="cuda") for _ in range(R)] if upload else pin
+    copy_stream = torch.cuda.Stream() if upload else None  # default priority
     ring_ev = collections.deque()  # (step, event), oldest first
     ctx_dev = torch.from_numpy(ctx0.astype(np.int32)).cuda()
 
@@ -1184,7 +1195,7 @@ def main():
     shared = cfg.ctx_kind == "shared_prefix"
     calls = []
     for n in range(total_steps):
-        hs, hc, hu, hp = views(pin[n % R])
+        hs, hc, hu, hp = views(dmeta[n % R])
         if one_launch:
             step_args = (spec, out, qs[n], ks[n], vs[n], hs, hc, cache.k, cache.v, tables, ctx_dev)
             calls.append((
@@ -1233,6 +1244,12 @@ def main():
         pu[:, 1] = nc
         pu[:, 2] = nb
         pp[:] = cows  # one (src, dst) row per token, (-1, -1) = no copy
+        if upload:
+            with torch.cuda.stream(copy_stream):
+                dmeta[r].copy_(pin[r], non_blocking=True)
+            ecp = torch.cuda.Event()
+            ecp.record(copy_stream)
+            stream.wait_event(ecp)
         h1 = time.perf_counter()
         plain, with_cow, decode = calls[n]
         append = with_cow if (cows[:, 0] >= 0).any() else plain
@@ -1367,7 +1384,8 @@ def main():
                    "sum_ctx_first_step": int(tok[0]), "units": units, "seed": cfg.seed,
                    "kv_loads": "cached (shared blocks)" if shared else "streamed (non-temporal)",
                    "step_launches": 1 if one_launch else 2,
-                   "hip_force_dev_kernarg": os.environ.get("HIP_FORCE_DEV_KERNARG")},
+                   "hip_force_dev_kernarg": os.environ.get("HIP_FORCE_DEV_KERNARG"),
+                   "step_metadata": args.metadata},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "shared_prefix_unique": unique,
         "us_per_step": round(wall / steps * 1e6, 2),
