@@ -1041,6 +1041,34 @@ def run_ceiling(args):
                                     "gbps": round(nbytes / t / 1e9, 1),
                                     "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)})
                     log(f"{results[-1]}")
+            # the gather through buffer loads with each cache-policy setting
+            if mode == "gather":
+                pol = lib.pa_probe_gather_read_policy
+                pol.restype = ctypes.c_int32
+                pol.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                ctypes.c_void_p]
+                for cp, name in ((0, "default"), (1, "sc0"), (2, "nt"), (3, "sc0 nt"), (16, "sc1"),
+                                 (17, "sc0 sc1"), (18, "sc1 nt"), (19, "sc0 sc1 nt")):
+                    times = []
+                    for rep in range(13):
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        rc = pol(k.data_ptr(), v.data_ptr(), n, od.data_ptr(), groups, per,
+                                 sink.data_ptr(), cp, stream.cuda_stream)
+                        e1.record(stream)
+                        if rc != 0:
+                            raise RuntimeError(f"probe launch failed ({rc})")
+                        torch.cuda.synchronize()
+                        if rep >= 3:
+                            times.append(e0.elapsed_time(e1) * 1e-3)
+                    t = float(np.median(times))
+                    results.append({"waves": groups * 8, "mode": mode,
+                                    "loads": f"buffer, policy {name}", "tiles_in_flight": 1,
+                                    "us": round(t * 1e6, 2), "gbps": round(nbytes / t / 1e9, 1),
+                                    "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)})
+                    log(f"{results[-1]}")
         del k, v
         torch.cuda.empty_cache()
     best = max(r["gbps"] for r in results if r["mode"] == "gather")

@@ -38,6 +38,17 @@ int32_t pa_probe_gather_read(const void* k, const void* v, int64_t num_chunks,
                              uint32_t* sink, int32_t nontemporal, int32_t in_flight,
                              void* stream);
 
+/*
+ * The same pattern (one tile in flight) through raw buffer loads whose cache-policy
+ * bits are cache_policy: bit 0 sc0, bit 1 nt, bit 4 sc1 (gfx950's load policy
+ * bits); one of 0, 1, 2, 3, 16, 17, 18, 19.  Each buffer must be under 2 GiB.
+ * Returns 0, or 1 for invalid arguments, 5 for a launch failure.
+ */
+int32_t pa_probe_gather_read_policy(const void* k, const void* v, int64_t num_chunks,
+                                    const int32_t* order, int32_t num_groups,
+                                    int32_t chunks_per_group, uint32_t* sink,
+                                    int32_t cache_policy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -150,7 +150,7 @@ def test_probe_library_exports_its_declared_function():
     src = open(os.path.join(ROOT, "include", "pagedkv_probe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     declared = sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src)))
-    assert declared == ["pa_probe_gather_read"]
+    assert declared == ["pa_probe_gather_read", "pa_probe_gather_read_policy"]
     lib = ctypes.CDLL(B.PROBE_LIB)
     fn = lib.pa_probe_gather_read
     fn.restype = ctypes.c_int32
@@ -160,3 +160,10 @@ def test_probe_library_exports_its_declared_function():
     assert fn(None, FAKE, 4, FAKE, 1, 1, FAKE, 1, 1, None) == 1          # null buffer
     assert fn(FAKE, FAKE, 4, FAKE, 1, 1, FAKE, 1, 3, None) == 1          # tiles in flight not 1 or 2
     assert fn(FAKE + 4, FAKE, 4, FAKE, 1, 1, FAKE, 1, 1, None) == 1      # misaligned
+    pol = lib.pa_probe_gather_read_policy
+    pol.restype = ctypes.c_int32
+    pol.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                    ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert pol(FAKE, FAKE, 4, FAKE, 1, 1, FAKE, 4, None) == 1            # policy not supported
+    assert pol(FAKE, FAKE, 1 << 16, FAKE, 1, 1, FAKE, 2, None) == 1      # buffer of 2 GiB
+    assert pol(None, FAKE, 4, FAKE, 1, 1, FAKE, 2, None) == 1            # null buffer
