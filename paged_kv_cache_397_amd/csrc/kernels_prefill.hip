@@ -347,8 +347,12 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int k = 0; k < NL; ++k) q[b][k] = *reinterpret_cast<const u32x4*>(qrow + 32 * k + 8 * j);
     }
-    // The pair maximum is taken on raw scores and scaled after, which needs c >= 0: for
-    // a negative scale, negate q (exact in bf16) and use -c, the same products.
+    // The pair maximum is taken on raw scores and scaled after, and masked keys carry
+    // a raw -inf that the scaling keeps -inf, which needs c > 0.  For a negative scale,
+    // negate q (exact in bf16) and use -c, the same products.  For a zero scale (every
+    // visible key weighs the same; -inf * 0 would be NaN) use the smallest normal
+    // float: a score under 2^26 in magnitude times it is under 2^-100, whose exp2 is 1
+    // in fp32, as for 0, and a masked key's weight stays 0.
     float cs = a.scale_log2e;
     if (cs < 0.f) {
         cs = -cs;
@@ -358,6 +362,7 @@ void prefill_kernel(PrefillArgs a) {
             for (int k = 0; k < NL; ++k) q[b][k] ^= 0x80008000u;
         }
     }
+    if (!(cs > 0.f)) cs = __FLT_MIN__;
     // Pairs below p_fast are visible to every column of the wave (both blocks
     // non-empty); the workgroup folds pairs 0 .. np - 1.
     int p_fast = 1 << 30;

@@ -44,14 +44,25 @@ def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what=""):
-    """Elementwise |gpu - ref| <= atol + rtol |ref|; reports max-abs / max-rel."""
+    """Elementwise |gpu - ref| <= atol + rtol |ref|, or equal (infinities of one
+    sign), or NaN on both sides; a NaN on one side only fails (a comparison with NaN
+    is false, so the test is written as what passes).  Returns max-abs / max-rel
+    over the finite differences (max-rel where |ref| >= 1e-3)."""
     atol, rtol = TOL[dtype]
-    err = np.abs(gpu - ref)
-    bad = err > atol + rtol * np.abs(ref)
-    big = np.abs(ref) >= 1e-3
-    max_abs = float(err.max()) if err.size else 0.0
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        err = np.abs(gpu - ref)
+        ok = ((np.isfinite(ref) & (err <= atol + rtol * np.abs(ref))) | (gpu == ref)
+              | (np.isnan(gpu) & np.isnan(ref)))
+    bad = ~ok
+    fin = np.isfinite(err)
+    big = fin & (np.abs(ref) >= 1e-3)
+    max_abs = float(err[fin].max()) if fin.any() else 0.0
     max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
-    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
+    nan_only = int((np.isnan(gpu) & ~np.isnan(ref)).sum())
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance "
+                           f"({nan_only} NaN where the oracle is not); "
                            f"max_abs={max_abs:.3g} max_rel={max_rel:.3g}")
     return max_abs, max_rel
 

@@ -312,3 +312,26 @@ def test_reused_workspace_across_calls():
             fresh = b.run(num_units=units)
             assert np.array_equal(to_storage(out).view(np.uint8), fresh.view(np.uint8)), (trial, units)
         assert_close(to_float64(fresh, "bf16"), b.expected(), "bf16", f"trial {trial}")
+
+
+@pytest.mark.parametrize("dtype,D,B,Hq,Hkv", [
+    ("bf16", 128, 16, 8, 8),   # per-head VALU path
+    ("bf16", 128, 16, 32, 8),  # group MFMA path, G = 4
+    ("f32", 64, 16, 4, 2),     # fp32
+])
+@pytest.mark.parametrize("sign", [-1.0, 0.0])
+def test_negative_and_zero_scale(dtype, D, B, Hq, Hkv, sign):
+    """The softmax takes any finite scale: a negative one (the largest weight goes to
+    the smallest product) and zero (every visible token weighs the same, so the row
+    is the mean of V) match the oracle on a poisoned cache."""
+    spec = ops.CacheSpec(num_blocks=64, block_size=B, num_kv_heads=Hkv, head_dim=D, dtype=dtype)
+    b = Batch(spec, EDGE_CTX[1:], Hq, seed=61, free_order=gen.pool_permutation(61, 64))
+    scale = sign / math.sqrt(D)
+    out = to_float64(b.run(scale=scale), dtype)
+    ref = b.expected(scale=scale)
+    assert_close(out, ref, dtype, f"scale {scale}")
+    if sign == 0.0:
+        for i, L in enumerate(b.ctx):
+            _, V = gen.seq_kv(61, i, int(L), Hkv, D, dtype)
+            mean = to_float64(V, dtype).mean(axis=0)        # [Hkv, D]
+            assert_close(out[i], np.repeat(mean, Hq // Hkv, axis=0), dtype, f"mean of V, seq {i}")

@@ -214,3 +214,27 @@ def test_rows_do_not_depend_on_the_rest_of_the_batch():
         torch.cuda.synchronize()
         alone = to_storage(out)
         assert np.array_equal(alone.view(np.uint16), together[r0:r0 + c].view(np.uint16)), s
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 4)])
+@pytest.mark.parametrize("sign", [-1.0, 0.0])
+def test_negative_and_zero_scale(Hq, Hkv, sign):
+    """A negative scale (the kernel negates q and takes maxima of the negated
+    products) and a zero scale (uniform weights over each row's visible keys) match
+    the oracle on ragged chunks."""
+    spec = ops.CacheSpec(num_blocks=640, block_size=16, num_kv_heads=Hkv, head_dim=128, dtype="bf16")
+    b = Chunks(spec, RAGGED, Hq, seed=62, free_order=gen.pool_permutation(62, 640))
+    scale = sign / math.sqrt(128)
+    out = torch.full((b.T, Hq, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ops.paged_attn_prefill(spec, out, b.q, b.cache.k, b.cache.v, b.tables,
+                           torch.from_numpy(b.qs).cuda(), torch.from_numpy(b.L).cuda(), scale)
+    torch.cuda.synchronize()
+    out = to_f64(to_storage(out), "bf16")
+    for s in range(b.S):
+        L, c = int(b.L[s]), int(b.c[s])
+        if c == 0:
+            continue
+        K, V = gen.seq_kv(62, s, L, Hkv, 128, "bf16")
+        ref = prefill_attention(to_f64(b.q_host[b.qs[s]:b.qs[s + 1]], "bf16"), to_f64(K, "bf16"),
+                                to_f64(V, "bf16"), scale, L - c)
+        assert_close(out[b.qs[s]:b.qs[s + 1]], ref, "bf16", f"scale {scale} seq {s}")
