@@ -68,16 +68,31 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     const uint32_t qmask = static_cast<uint32_t>(__ballot(qstart));
     const uint32_t valid = static_cast<uint32_t>(__ballot(my >= 0)) & 0xffffu;
     const uint32_t covered = (qmask | (qmask << 1) | (qmask << 2) | (qmask << 3)) & 0xffffu;
-    // K of every token, and V rows into LDS: lane covers (token r, 16-byte chunk c)
-    for (int g = lane; g < TW * KG; g += kWaveSize) {
-        const int r = g / KG, c = g % KG;
+    // K of every token, and V rows into LDS: piece `it` of a lane is (token r, 16-byte
+    // chunk c).  Every load is issued, unconditionally, before the first store, so a
+    // wave has all of its window's reads in flight at once (a loop that stores each
+    // piece before loading the next keeps one pair in flight); a row past the last
+    // token reads the last token's row instead (in bounds, never stored).
+    constexpr int NI = TW * KG / kWaveSize;
+    static_assert(NI * kWaveSize == TW * KG, "pieces per lane");
+    u32x4 kr[NI], vr[NI];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+        const int g = lane + it * kWaveSize, r = g / KG, c = g % KG;
+        const int row = min(t0 + r, num_tokens - 1);
+        const size_t src = (static_cast<size_t>(row) * num_kv_heads + h) * D + c * X;
+        kr[it] = *reinterpret_cast<const u32x4*>(k + src);
+        vr[it] = *reinterpret_cast<const u32x4*>(v + src);
+    }
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+        const int g = lane + it * kWaveSize, r = g / KG, c = g % KG;
         const long long tbr = __shfl(tb, r);
         const int tir = __shfl(ti, r);
-        if (!((valid >> r) & 1u)) continue;
-        const size_t src = (static_cast<size_t>(t0 + r) * num_kv_heads + h) * D + c * X;
-        *reinterpret_cast<u32x4*>(k_cache + tbr + (c * tt + tir) * X) =
-            *reinterpret_cast<const u32x4*>(k + src);
-        *reinterpret_cast<u32x4*>(&vrow[r][c * X]) = *reinterpret_cast<const u32x4*>(v + src);
+        if ((valid >> r) & 1u) {
+            *reinterpret_cast<u32x4*>(k_cache + tbr + (c * tt + tir) * X) = kr[it];
+            *reinterpret_cast<u32x4*>(&vrow[r][c * X]) = vr[it];
+        }
     }
     __syncthreads();
     // V of each quad: group (m, j, i) holds dims 16E*m + 16e + i (e < E) of its 4 tokens
