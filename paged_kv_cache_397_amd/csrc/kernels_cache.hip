@@ -222,6 +222,16 @@ __global__ __launch_bounds__(D) void append_tokens_kernel(
     // from pinned host memory, each dependent read would cost a host-link round trip.
     const bool tok = t < num_tokens;
     const int64_t slot = tok ? slots[t] : -1;
+    // The token's K and V (device memory) are requested beside the slot (possibly a
+    // host-link read), not after it: they do not depend on it.
+    const int d = tid;
+    const size_t src = (static_cast<size_t>(tok ? t : 0) * num_kv_heads + h) * D;
+    T vval{};
+    u32x4 kval{};
+    if (tok) {
+        vval = v[src + d];
+        if (d % X == 0) kval = *reinterpret_cast<const u32x4*>(k + src + d);
+    }
     const int n0 = wg * D + tid;
     const int ur = n0 < num_updates ? upd[3 * n0] : -1;
     const int uc = n0 < num_updates ? upd[3 * n0 + 1] : -1;
@@ -242,15 +252,12 @@ __global__ __launch_bounds__(D) void append_tokens_kernel(
     const int o = static_cast<int>(slot - b * block_size);
     const int ti = o % tt;
     const int j = ti >> 2, r = ti & 3;
-    const int d = tid;
     const size_t tile_base =
         ((static_cast<size_t>(b) * tpb + o / tt) * num_kv_heads + h) * (static_cast<size_t>(tt) * D);
-    const size_t src = (static_cast<size_t>(t) * num_kv_heads + h) * D;
     const int m = d / (16 * E), ee = (d >> 4) % E, i = d & 15;
-    v_cache[tile_base + ((((m * (tt / 4) + j) * 16 + i) * E + ee) * 4 + r)] = v[src + d];
+    v_cache[tile_base + ((((m * (tt / 4) + j) * 16 + i) * E + ee) * 4 + r)] = vval;
     if (d % X == 0)
-        *reinterpret_cast<u32x4*>(k_cache + tile_base + ((d / X) * tt + ti) * X) =
-            *reinterpret_cast<const u32x4*>(k + src + d);
+        *reinterpret_cast<u32x4*>(k_cache + tile_base + ((d / X) * tt + ti) * X) = kval;
 }
 
 template <typename T, int D>
