@@ -133,7 +133,24 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     }
 }
 
-// Grid (pairs, 2 arrays, chunks); 256 threads copy 16 bytes each per chunk.
+// The 16-byte pieces idx = n + 256 k (k < 4) of one block that a thread moves:
+// all four loads are issued before the first store (a piece past the block's end
+// loads the block's last piece instead, in bounds, and is not stored), so that a
+// thread keeps four requests in flight rather than one.
+__device__ __forceinline__ void move_four(const u32x4* __restrict__ s, u32x4* __restrict__ d,
+                                          int64_t n, int64_t block_u4) {
+    u32x4 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = s[min(n + k * 256, block_u4 - 1)];
+    // all four values are taken here, so the compiler cannot sink a load into the
+    // store that uses it (it would wait for each in turn)
+    asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (n + k * 256 < block_u4) d[n + k * 256] = r[k];
+}
+
+// Grid (pairs, 2 arrays, chunks); 256 threads copy 16 bytes each per 4 KiB of a chunk.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_cache,
                                                           u32x4* __restrict__ v_cache,
                                                           const int32_t* __restrict__ pairs,
@@ -143,13 +160,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
     u32x4* base = blockIdx.y == 0 ? k_cache : v_cache;
     const int64_t n = static_cast<int64_t>(blockIdx.z) * 1024 + threadIdx.x;
-    const u32x4* s = base + src * block_u4;
-    u32x4* dp = base + dst * block_u4;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int64_t idx = n + k * 256;
-        if (idx < block_u4) dp[idx] = s[idx];
-    }
+    if (n >= block_u4) return;
+    move_four(base + src * block_u4, base + dst * block_u4, n, block_u4);
 }
 
 // Whole-block copies between two pools of the same block geometry - HBM and pinned
@@ -168,20 +180,10 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(const u32x4* __restric
     const int src = pairs[2 * blockIdx.x];
     const int dst = pairs[2 * blockIdx.x + 1];
     if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
-    const u32x4* s = (blockIdx.y == 0 ? src_k : src_v) + src * block_u4;
-    u32x4* d = (blockIdx.y == 0 ? dst_k : dst_v) + dst * block_u4;
     const int64_t n = static_cast<int64_t>(blockIdx.z) * 1024 + threadIdx.x;
-    u32x4 r[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int64_t idx = n + k * 256;
-        if (idx < block_u4) r[k] = s[idx];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int64_t idx = n + k * 256;
-        if (idx < block_u4) d[idx] = r[k];
-    }
+    if (n >= block_u4) return;
+    move_four((blockIdx.y == 0 ? src_k : src_v) + src * block_u4,
+              (blockIdx.y == 0 ? dst_k : dst_v) + dst * block_u4, n, block_u4);
 }
 
 __global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict__ tables, int rows,
