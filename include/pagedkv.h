@@ -183,6 +183,8 @@ enum {
  * slot t % B ([P1] sections 2 and 2.2: decode attends over every cached token
  * of the sequence, gathered from its scattered blocks; section 2.3 item 3:
  * ragged lengths).  L == 0 gives zeros.  No causal, sliding or bias mask.
+ * scale is any finite value (zero gives uniform weights over the L tokens; a
+ * negative scale is accepted); NaN or infinity gives PA_ERR_INVALID_ARG.
  *
  *   out            device, [num_seqs, Hq, D], dtype of the cache, 16-B aligned
  *   q              device, [num_seqs, Hq, D], dtype of the cache, 16-B aligned
@@ -344,6 +346,8 @@ pa_status pa_paged_attn_decode_noalloc(const pa_cache_desc* desc, void* out, con
  *   context_lens   device, [num_seqs] int32, clamped to [0, max_blocks_per_seq * B]
  *   max_query_len  host; every c_s must be <= it (it sizes the grid: rows past
  *                  it may be left unwritten)
+ * scale: any finite value, zero and negative included (NaN or infinity gives
+ * PA_ERR_INVALID_ARG).
  * Rows of a chunk longer than its cache (positions below 0) are written as
  * zeros; rows whose query_start entries are out of range are not written.
  * Block IDs outside [0, N) in a column that is read are replaced by 0.
