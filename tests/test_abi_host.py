@@ -71,6 +71,7 @@ def _decode(**kw):
     (dict(units=-2), N.PA_ERR_INVALID_ARG),
     (dict(wsb=16), N.PA_ERR_INVALID_ARG),                # workspace too small
     (dict(scale=float("nan")), N.PA_ERR_INVALID_ARG),
+    (dict(scale=float("-inf")), N.PA_ERR_INVALID_ARG),
     (dict(flags=2), N.PA_ERR_INVALID_ARG),               # unknown flag bit
     (dict(flags=1, out=None), N.PA_ERR_INVALID_ARG),     # PA_DECODE_KEEP_CACHED is accepted
     (dict(maxB=0), N.PA_ERR_INVALID_ARG),
