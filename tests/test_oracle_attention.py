@@ -202,3 +202,22 @@ def test_unused_slots_and_table_entries_are_not_read():
     padded = np.where(tables >= 0, tables, 10 ** 6)
     out = paged_decode(layout, q, kcn, vcn, padded, ctx, 0.125)
     assert np.array_equal(out, base)
+
+
+def test_zero_and_negative_scales():
+    """scale = 0 weighs every token equally (the mean of V); a negative scale is the
+    positive one with the query negated; two tokens at a negative scale follow the
+    logistic weights of the negated score difference."""
+    rng = gen.stream(5, 9)
+    q = rng.standard_normal((4, 32))
+    K = rng.standard_normal((23, 2, 32))
+    V = rng.standard_normal((23, 2, 32))
+    np.testing.assert_allclose(decode_attention(q, K, V, 0.0), np.repeat(V.mean(axis=0), 2, axis=0),
+                               rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(decode_attention(q, K, V, -0.3), decode_attention(-q, K, V, 0.3),
+                               rtol=1e-13, atol=1e-14)
+    s = -0.5 * (K[:2, 0] @ q[0])
+    w1 = 1.0 / (1.0 + math.exp(s[0] - s[1]))
+    expect = (1.0 - w1) * V[0, 0] + w1 * V[1, 0]
+    np.testing.assert_allclose(decode_attention(q[:1], K[:2, :1], V[:2, :1], -0.5)[0], expect,
+                               rtol=1e-13, atol=1e-14)

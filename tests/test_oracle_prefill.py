@@ -176,3 +176,16 @@ def test_prefill_pins_reject_mutants(mutant, monkeypatch):
                            to_float64(Vs[i], dtype), 0.125, L - c)
         bad |= not np.allclose(out[rows], ref, rtol=1e-6, atol=1e-6)
     assert bad, mutant.__name__
+
+
+def test_zero_scale_gives_running_mean():
+    """A zero scale equalises the scores whatever the query: row i is the mean of
+    the value rows 0 .. start + i."""
+    rng = gen.stream(33, 7)
+    Hq, Hkv, D, L, start = 4, 2, 32, 27, 9
+    V = rng.standard_normal((L, Hkv, D))
+    K = rng.standard_normal((L, Hkv, D))
+    q = rng.standard_normal((L - start, Hq, D))
+    out = prefill_attention(q, K, V, 0.0, start)
+    cum = np.cumsum(V, axis=0) / np.arange(1, L + 1)[:, None, None]
+    np.testing.assert_allclose(out, np.repeat(cum[start:], Hq // Hkv, axis=1), rtol=1e-13, atol=1e-13)
