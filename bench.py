@@ -1204,11 +1204,19 @@ def main():
         return (buf[:2 * S].view(torch.int64), buf[2 * S:3 * S], buf[3 * S:6 * S].view(S, 3),
                 buf[6 * S:8 * S].view(S, 2))
 
+    # numpy views of every pinned slot, and the allocator's append bound to each slot:
+    # slots and copy-on-write pairs land in the slot, new table entries in two arrays
+    pin_np = [tuple(x.numpy() for x in views(buf)) for buf in pin]
+    new_blocks = np.empty(S, dtype=np.int32)
+    new_cols = np.empty(S, dtype=np.int32)
+    binds = [cache.alloc.bind_append_batch(seq_ids, ps, pp, new_blocks, new_cols)
+             for ps, _, _, pp in pin_np]
+
     ctx_now = ctx0.astype(np.int64).copy()
     stream = torch.cuda.current_stream()
     kv_per_tok = cfg.kv_bytes_per_token()
     ev = []
-    host = []  # per timed step: (host bookkeeping + staging, whole host side) seconds
+    host = []  # per timed step: (allocator, ring-slot wait, staging, whole host side) seconds
 
     # Every launch of every step is bound once (arguments converted up front); the
     # per-step metadata has a fixed shape (a copy-on-write row and a table-update row
@@ -1248,13 +1256,9 @@ def main():
         the decode (measured: 2.3 us per step), so the other steps record at most the
         ring-slot event, after the decode."""
         h0 = time.perf_counter()
-        # a1: host bookkeeping in the library allocator
-        st, done, slots, cows, nb, nc = cache.alloc.append_batch(seq_ids)
-        if st != 0 or done != S:
-            raise RuntimeError(f"append_batch failed at step {n}: status {st}")
-        ctx_now[:] += 1
-        ha = time.perf_counter()
-        # a2: the step's metadata into a pinned ring slot the write kernel reads in place
+        # The step's metadata goes into pinned ring slot n % R, which the write kernel
+        # reads in place; first wait until the launches of step n - R, its last user,
+        # are done.
         r = n % R
         if n >= R:
             while ring_ev[0][0] < n - R:
@@ -1265,13 +1269,19 @@ def main():
             while not ring_ev[0][1].query():
                 pass
         hw = time.perf_counter()
-        ps, pc, pu, pp = (x.numpy() for x in views(pin[r]))
-        ps[:] = slots
+        # a1: host bookkeeping in the library allocator, which writes every sequence's
+        # slot and copy-on-write pair straight into the ring slot
+        st, done = binds[r]()
+        if st != 0 or done != S:
+            raise RuntimeError(f"append_batch failed at step {n}: status {st}")
+        ctx_now[:] += 1
+        ha = time.perf_counter()
+        # a2: the rest of the step's metadata (lengths, table updates) into the slot
+        ps, pc, pu, pp = pin_np[r]
         pc[:] = ctx_now
-        pu[:, 0] = np.where(nb >= 0, seq_ids, -1)  # (row, column, block); row -1 = no update
-        pu[:, 1] = nc
-        pu[:, 2] = nb
-        pp[:] = cows  # one (src, dst) row per token, (-1, -1) = no copy
+        pu[:, 0] = np.where(new_blocks >= 0, seq_ids, -1)  # (row, column, block); row -1 = no update
+        pu[:, 1] = new_cols
+        pu[:, 2] = new_blocks
         if upload:
             with torch.cuda.stream(copy_stream):
                 dmeta[r].copy_(pin[r], non_blocking=True)
@@ -1280,7 +1290,7 @@ def main():
             stream.wait_event(ecp)
         h1 = time.perf_counter()
         plain, with_cow, decode = calls[n]
-        append = with_cow if (cows[:, 0] >= 0).any() else plain
+        append = with_cow if (pp[:, 0] >= 0).any() else plain  # (-1, -1) = no copy
         if decode is None:  # one launch: the step call does the writes and the decode
             append, decode = (lambda: None), append
         timing = mode == "profile" or (mode == "timed" and (n - warm) % 5 == 0)
@@ -1310,7 +1320,7 @@ def main():
         if mode == "timed":
             step_tok.append(int(ctx_now.sum()))
             # (allocator, waiting for the ring slot, staging the metadata, whole host side)
-            host.append((ha - h0, hw - ha, h1 - hw, time.perf_counter() - h0))
+            host.append((ha - hw, hw - h0, h1 - ha, time.perf_counter() - h0))
 
     ev = {"timed": [], "profile": []}
     step_tok = []  # sum of context lengths of every timed step
@@ -1444,9 +1454,11 @@ def main():
         "host_ring_wait_us_median": round(float(np.median([h[1] for h in host])) * 1e6, 2),
         "host_step_us_median": round(float(np.median([h[3] for h in host])) * 1e6, 2),
         "host_step_us_max": round(float(np.max([h[3] for h in host])) * 1e6, 2),
-        "host_note": "bookkeeping = the library allocator reserving every sequence's next slot; "
-                     "staging = writing the step's metadata into its pinned ring slot; ring wait = "
-                     "waiting for the GPU to free that slot (the host runs ahead of the GPU)",
+        "host_note": "ring wait = waiting for the GPU to free the step's pinned ring slot (the "
+                     "host runs ahead of the GPU); bookkeeping = the library allocator reserving "
+                     "every sequence's next slot, its slots and copy-on-write pairs written "
+                     "straight into the ring slot; staging = the rest of the step's metadata "
+                     "(lengths, table updates) into the slot",
         "roofline": {
             "kernel": ("decode_pass1, decode-step form (the step's cache writes, gather + attention, "
                        "merge of split sequences, one cooperative launch)" if one_launch else

@@ -138,6 +138,33 @@ class BlockAllocator:
             N.check(st, "seq_append_batch")
         return st, done.value, slots, cows, nb, nc
 
+    def bind_append_batch(self, seqs, slots, cow_pairs, new_blocks, new_cols):
+        """append_batch for a fixed list of sequences, with its outputs written into
+        the given arrays (int64 [n], int32 [n, 2], int32 [n], int32 [n]; C-contiguous,
+        e.g. views of a pinned staging buffer).  The arguments are converted once; the
+        returned callable makes one library call per step and returns (status, done).
+        The arrays must outlive the callable."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = seqs.shape[0]
+        for arr, dt, shape in ((slots, np.int64, (n,)), (cow_pairs, np.int32, (n, 2)),
+                               (new_blocks, np.int32, (n,)), (new_cols, np.int32, (n,))):
+            if arr.dtype != dt or arr.shape != shape or not arr.flags.c_contiguous:
+                raise ValueError(f"output array must be C-contiguous {np.dtype(dt).name} {shape}")
+        done = ctypes.c_int32()
+        fn = self._lib.pa_seq_append_batch
+        args = (self._h, _ptr(seqs), n, _ptr(slots), _ptr(cow_pairs), _ptr(new_blocks),
+                _ptr(new_cols), ctypes.byref(done))
+        keep = (seqs, slots, cow_pairs, new_blocks, new_cols)
+
+        def call():
+            st = fn(*args)
+            if st not in (N.PA_OK, N.PA_ERR_OOM, N.PA_ERR_STATE):
+                N.check(st, "seq_append_batch")
+            return st, done.value
+
+        call.keep = keep  # the arrays the pointers refer to
+        return call
+
     def fork(self, parent: int, child: int) -> None:
         N.check(self._lib.pa_seq_fork(self._h, parent, child), "seq_fork")
 
