@@ -150,7 +150,8 @@ __device__ __forceinline__ void move_four(const u32x4* __restrict__ s, u32x4* __
         if (n + k * 256 < block_u4) d[n + k * 256] = r[k];
 }
 
-// Grid (pairs, 2 arrays, chunks); 256 threads copy 16 bytes each per 4 KiB of a chunk.
+// Grid (pairs, 2 arrays, 16 KiB chunks of a block); each of 256 threads moves four
+// 16-byte pieces of its chunk.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_cache,
                                                           u32x4* __restrict__ v_cache,
                                                           const int32_t* __restrict__ pairs,
