@@ -93,11 +93,11 @@ def copy_calibration(mib: int):
 ROOT = os.path.dirname(os.path.abspath(__file__))
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_397_amd", "csrc", f)
                   for f in ("decode_kernels.h", "decode_variant.hip", "kernels_decode.hip",
-                            "kernels_common.h")]
+                            "kernels_common.h", "pagedkv_internal.h")]
 
 
 PREFILL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_397_amd", "csrc", f)
-                   for f in ("kernels_prefill.hip", "kernels_common.h")]
+                   for f in ("kernels_prefill.hip", "kernels_common.h", "pagedkv_internal.h")]
 
 
 def measured_traffic(config_name: str, kind: str = "decode", sources=None):

@@ -932,6 +932,9 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         T_row = s_tw[0];
         W_row = s_tw[1];
     }
+    // Per-head path: whether the workgroup's rows meet at every tile (below); the
+    // same for every wave of the workgroup, since T_row is.
+    const bool tile_barrier = T_row >= kBarrierTilesPerSeq * static_cast<long long>(S);
     int32_t* rec = a.unit_rec + static_cast<size_t>(u) * kRecInts;
     if (lane == 0) rec[0] = -1;  // set below when a split sequence ends in this unit
     // The unit's tiles: n_tiles from tile tin of row row0, starting in sequence seq0 at
@@ -1141,10 +1144,16 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         // The rows of a workgroup walk the same tiles; meeting once per tile keeps
         // their requests for one block's adjacent heads (consecutive 4 KiB pieces of
         // K and of V) reaching memory together.  Measured with streamed loads, that
-        // pays for the per-head path (G = 1: 343 against 352 us on a batch of 64
-        // 32-head sequences) but not for the group path (G = 4: 220 us without it
-        // against 221 with it on a batch of 256), which therefore runs without it.
-        if constexpr (NW > 1 && Path::GH == 1) __syncthreads();
+        // pays for the per-head path on long sequences (G = 1: 344 against 353 us on
+        // a batch of 64 32-head sequences of 2112 tokens on average) but not on many
+        // short ones, whose ranges cross many sequence ends (1079 against 1089 us of
+        // attention per step without it over about 690 40-head sequences of about 600
+        // tokens), so the per-head path meets only when the batch averages
+        // kBarrierTilesPerSeq tiles or more per sequence.  The group path never meets
+        // (G = 4: 220 us without it against 221 with it on a batch of 256).
+        if constexpr (NW > 1 && Path::GH == 1) {
+            if (tile_barrier) __syncthreads();
+        }
         while (kf == ch.n) {  // chunk used up: describe the next tiles (empty chunks only
                               // arise from runs of sequences with no cached tokens)
             if (ch.next.row >= a.rows) {
