@@ -934,7 +934,7 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
     }
     // Per-head path: whether the workgroup's rows meet at every tile (below); the
     // same for every wave of the workgroup, since T_row is.
-    const bool tile_barrier = T_row >= kBarrierTilesPerSeq * static_cast<long long>(S);
+    const bool tile_barrier = !Stream || T_row >= kBarrierTilesPerSeq * static_cast<long long>(S);
     int32_t* rec = a.unit_rec + static_cast<size_t>(u) * kRecInts;
     if (lane == 0) rec[0] = -1;  // set below when a split sequence ends in this unit
     // The unit's tiles: n_tiles from tile tin of row row0, starting in sequence seq0 at
@@ -1148,9 +1148,12 @@ __global__ __launch_bounds__(64 * NW) void decode_pass1(DecodeArgs a) {
         // a batch of 64 32-head sequences of 2112 tokens on average) but not on many
         // short ones, whose ranges cross many sequence ends (1079 against 1089 us of
         // attention per step without it over about 690 40-head sequences of about 600
-        // tokens), so the per-head path meets only when the batch averages
-        // kBarrierTilesPerSeq tiles or more per sequence.  The group path never meets
-        // (G = 4: 220 us without it against 221 with it on a batch of 256).
+        // tokens), so with streamed loads the per-head path meets only when the batch
+        // averages kBarrierTilesPerSeq tiles or more per sequence.  With cached loads
+        // (blocks shared between sequences) it always meets: on a prefix-cached
+        // serving trace of sequences as short, 1135 against 1176 us of attention per
+        // step with it.  The group path never meets (G = 4: 220 us without it against
+        // 221 with it on a batch of 256).
         if constexpr (NW > 1 && Path::GH == 1) {
             if (tile_barrier) __syncthreads();
         }

@@ -88,8 +88,9 @@ constexpr int kStepSpinLimit = 1 << 20;
 // sequence (piece) in its range, so a piece is charged one tile.
 constexpr int kTileCost = 4;
 constexpr int kPieceCost = 4;
-// Per-head decode: the rows of a workgroup meet at every tile when the batch averages
-// at least this many 16-token tiles per sequence (long walks); otherwise they run free.
+// Per-head decode with streamed loads: the rows of a workgroup meet at every tile when
+// the batch averages at least this many 16-token tiles per sequence (long walks);
+// otherwise they run free.  With cached loads they always meet.
 constexpr int kBarrierTilesPerSeq = 64;
 
 // Floats of one partial-result record: heads_per_row * (D accumulators + max + sum).
